@@ -133,8 +133,9 @@ def process(z_raw: np.ndarray, T: float, top_k: int = 0, top_p: float = 1.0) -> 
     near = False
     # top-p: shortest prefix of whole tie groups (descending value) with mass >= P
     if 0.0 < top_p < 1.0:
-        values = np.unique(z[kept])[::-1]          # distinct values, descending
-        group_mass = np.array([p[kept & (z == v)].sum() for v in values])
+        values, group = np.unique(z[kept], return_inverse=True)   # ascending
+        group_mass = np.bincount(group, weights=p[kept], minlength=values.shape[0])
+        values, group_mass = values[::-1], group_mass[::-1]       # descending
         G = np.cumsum(group_mass)
         reach = np.nonzero(G >= top_p)[0]
         J = int(reach[0]) if reach.size else len(values) - 1
