@@ -1,0 +1,230 @@
+"""Thin Python binding of libspecverify.so (argument marshalling only).
+
+Every step of the verify runs in the library's HIP kernels; this module only
+turns torch tensors into device pointers, allocates outputs and the workspace
+with torch on the tensors' device, and passes torch's current stream.  It
+raises when the library is missing: there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+
+SV_F32, SV_BF16 = 0, 1
+ONEHOT, LOGITS, PROBS = 0, 1, 2
+ROW_OK, ROW_NONFINITE, ROW_EMPTY, ROW_BAD_K, ROW_BAD_TOKEN, ROW_BAD_PARAM = range(6)
+MAX_K = 63
+
+_lib = None
+_lock = threading.Lock()
+_ws_cache: dict = {}
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+
+
+class SpecVerifyError(RuntimeError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    """Load libspecverify.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise SpecVerifyError(
+                        f"{LIB_PATH} is missing; build it with "
+                        "`python -m lossless_rejection_sampling_spec_amd.build`")
+                L = ctypes.CDLL(LIB_PATH)
+                L.spec_verify_abi_version.restype = _i32
+                L.spec_verify_abi_version.argtypes = []
+                L.spec_verify_status_string.restype = ctypes.c_char_p
+                L.spec_verify_status_string.argtypes = [_i32]
+                L.spec_verify_workspace_bytes.restype = _sz
+                L.spec_verify_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
+                L.spec_verify_workspace_init.restype = _i32
+                L.spec_verify_workspace_init.argtypes = [_vp, _sz, _vp]
+                L.spec_verify_greedy.restype = _i32
+                L.spec_verify_greedy.argtypes = [
+                    _vp, _i32, _i64, _vp, _vp, _i32, _i32, _i32, _i32,
+                    _vp, _vp, _vp, _vp, _sz, _vp]
+                L.spec_verify_sampled.restype = _i32
+                L.spec_verify_sampled.argtypes = [
+                    _vp, _i32, _i64, _vp, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                    _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+                _lib = L
+    return _lib
+
+
+def abi_version() -> int:
+    return int(lib().spec_verify_abi_version())
+
+
+def status_string(code: int) -> str:
+    return lib().spec_verify_status_string(int(code)).decode()
+
+
+def workspace_bytes(batch: int, total_rows: int, vocab: int, max_k: int) -> int:
+    return int(lib().spec_verify_workspace_bytes(batch, total_rows, vocab, max_k))
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SV_F32
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    raise ValueError(f"unsupported logit dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _check_rows(t: torch.Tensor, name: str) -> None:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit stride along the vocabulary")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def _check_vec(t: torch.Tensor | None, name: str, dtype, n: int | None = None) -> None:
+    if t is None:
+        return
+    if t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} device tensor")
+    if n is not None and t.numel() < n:
+        raise ValueError(f"{name} needs at least {n} elements")
+
+
+def get_workspace(device: torch.device, nbytes: int) -> torch.Tensor:
+    """A zero-initialised workspace cached per device (the library leaves it
+    ready after every call, so it is reused without clearing)."""
+    key = (device.type, device.index)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def _raise(rc: int) -> None:
+    if rc != 0:
+        raise ValueError(f"spec_verify: {status_string(rc)} (code {rc})")
+
+
+def verify_greedy(target: torch.Tensor, cu_seqlens: torch.Tensor, draft_tokens: torch.Tensor,
+                  *, max_k: int, vocab: int | None = None, workspace: torch.Tensor | None = None,
+                  out: tuple | None = None):
+    """Greedy prefix-match verify.  Returns (accepted[B], out_tokens[R], status[B])."""
+    _check_rows(target, "target")
+    dev = target.device
+    batch = cu_seqlens.numel() - 1
+    total_rows = target.shape[0]
+    V = target.shape[1] if vocab is None else int(vocab)
+    _check_vec(cu_seqlens, "cu_seqlens", torch.int32, batch + 1)
+    _check_vec(draft_tokens, "draft_tokens", torch.int32)
+    if out is None:
+        accepted = torch.empty(batch, dtype=torch.int32, device=dev)
+        tokens = torch.empty(total_rows, dtype=torch.int32, device=dev)
+        status = torch.empty(batch, dtype=torch.int32, device=dev)
+    else:
+        accepted, tokens, status = out
+    need = workspace_bytes(batch, total_rows, V, max_k)
+    if need == 0:
+        raise ValueError("invalid sizes for spec_verify_greedy")
+    ws = get_workspace(dev, need) if workspace is None else workspace
+    rc = lib().spec_verify_greedy(
+        _ptr(target), _dtype_code(target), target.stride(0), _ptr(cu_seqlens),
+        _ptr(draft_tokens) if draft_tokens.numel() else None, batch, total_rows, max_k, V,
+        _ptr(accepted), _ptr(tokens), _ptr(status), _ptr(ws), ws.numel(), _stream(dev))
+    _raise(rc)
+    return accepted, tokens, status
+
+
+def verify_sampled(target: torch.Tensor, draft: torch.Tensor | None, draft_kind: torch.Tensor,
+                   cu_seqlens: torch.Tensor, draft_tokens: torch.Tensor, uniforms: torch.Tensor,
+                   temperature: torch.Tensor, top_k: torch.Tensor | None = None,
+                   top_p: torch.Tensor | None = None, *, max_k: int, vocab: int | None = None,
+                   want_probs: bool = False, workspace: torch.Tensor | None = None,
+                   out: tuple | None = None):
+    """Sampled verify by rejection sampling (greedy requests mixed in).
+
+    Returns (accepted[B], out_tokens[R], status[B], p_at_draft, q_at_draft);
+    the last two are None unless want_probs."""
+    _check_rows(target, "target")
+    dev = target.device
+    batch = cu_seqlens.numel() - 1
+    total_rows = target.shape[0]
+    V = target.shape[1] if vocab is None else int(vocab)
+    n_draft = total_rows - batch
+    if draft is not None:
+        _check_rows(draft, "draft")
+    _check_vec(cu_seqlens, "cu_seqlens", torch.int32, batch + 1)
+    _check_vec(draft_kind, "draft_kind", torch.int32, batch)
+    _check_vec(draft_tokens, "draft_tokens", torch.int32, n_draft)
+    _check_vec(uniforms, "uniforms", torch.float32, total_rows)
+    _check_vec(temperature, "temperature", torch.float32, batch)
+    _check_vec(top_k, "top_k", torch.int32, batch)
+    _check_vec(top_p, "top_p", torch.float32, batch)
+    if out is None:
+        accepted = torch.empty(batch, dtype=torch.int32, device=dev)
+        tokens = torch.empty(total_rows, dtype=torch.int32, device=dev)
+        status = torch.empty(batch, dtype=torch.int32, device=dev)
+        p_at = torch.empty(max(n_draft, 1), dtype=torch.float32, device=dev) if want_probs else None
+        q_at = torch.empty(max(n_draft, 1), dtype=torch.float32, device=dev) if want_probs else None
+    else:
+        accepted, tokens, status, p_at, q_at = out
+    need = workspace_bytes(batch, total_rows, V, max_k)
+    if need == 0:
+        raise ValueError("invalid sizes for spec_verify_sampled")
+    ws = get_workspace(dev, need) if workspace is None else workspace
+    rc = lib().spec_verify_sampled(
+        _ptr(target), _dtype_code(target), target.stride(0),
+        _ptr(draft), _dtype_code(draft) if draft is not None else SV_F32,
+        draft.stride(0) if draft is not None else 0,
+        _ptr(draft_kind), _ptr(cu_seqlens), _ptr(draft_tokens) if n_draft else None,
+        _ptr(uniforms), _ptr(temperature), _ptr(top_k), _ptr(top_p),
+        batch, total_rows, max_k, V, _ptr(accepted), _ptr(tokens), _ptr(p_at), _ptr(q_at),
+        _ptr(status), _ptr(ws), ws.numel(), _stream(dev))
+    _raise(rc)
+    return accepted, tokens, status, p_at, q_at
+
+
+def workload_tensors(w, device) -> dict:
+    """Device tensors of a synthetic workload (see synth.Workload)."""
+    def rows(a, dt):
+        if a is None:
+            return None
+        if dt == SV_BF16:
+            return torch.from_numpy(a.view("int16")).to(device).view(torch.bfloat16)
+        return torch.from_numpy(a).to(device)
+
+    def vec(a, dtype):
+        return None if a is None else torch.from_numpy(a).to(device=device, dtype=dtype)
+
+    return dict(
+        target=rows(w.target, w.target_dtype),
+        draft=rows(w.draft, w.draft_dtype),
+        draft_kind=vec(w.draft_kind, torch.int32),
+        cu_seqlens=vec(w.cu_seqlens, torch.int32),
+        draft_tokens=vec(w.draft_tokens, torch.int32),
+        uniforms=vec(w.uniforms, torch.float32),
+        temperature=vec(w.temperature, torch.float32),
+        top_k=vec(w.top_k, torch.int32),
+        top_p=vec(w.top_p, torch.float32),
+    )

@@ -1,0 +1,1664 @@
+// specverify.hip -- HIP kernels and C ABI of the batched speculative-decoding
+// verify (see include/specverify.h for the contract of every entry point).
+//
+// Written for MI355X (gfx950): wave64, 256-thread workgroups, 128-bit global
+// loads, NaN-propagating 3-input max, no matrix cores (the verify is a
+// bandwidth-bound stream over vocabulary rows).
+//
+// One fused kernel, k_verify, does the whole verify of a batch:
+//   producers   workgroup (b, j, s) reads a strip of S chunks (CHUNK elements
+//               each) of target row j of request b -- and of draft row j when
+//               the request's drafts are logits -- once from HBM and publishes
+//               per-chunk statistics (max, sum of exp2 terms, or argmax).
+//   finalizer   the last producer of a request in launch order waits for the
+//               request's statistics, merges them in a fixed order, runs the
+//               acceptance scan as a 64-lane ballot (lane j = position j),
+//               writes the outputs, and draws the final token itself when that
+//               needs only the target row (bonus draw, one-hot draft
+//               rejection); greedy requests end here.
+//   helpers     nc workgroups per logit/probability-draft request, launched
+//               right after the next request's producers: when the finalizer
+//               reports a rejection they compute the residual mass
+//               max(0, p - q) of one chunk each; the last one picks the chunk
+//               that holds u * W, re-reads it and draws the token.
+// k_thresh (only when top-k / top-p arrays are given) runs first and computes
+// each filtered row's raw-logit threshold tau (kept iff l >= tau).
+//
+// Hand-off between workgroups.  Every value one workgroup passes to another
+// travels in a 64-bit word whose top bit is a "fresh" tag: the writer stores
+// the word with one agent-scope atomic store (coherent across the eight XCD
+// L2 caches, no fence, no counter), the single reader of that word waits for
+// the tag, takes the payload and stores the word back without its tag.  Every
+// wait is on a workgroup with a smaller launch index, and every wait is
+// bounded (a request whose wait runs out reports SV_ROW_INTERNAL).  A
+// workspace is therefore left with no tag set when a call ends.
+//
+// Numerics (temperature T, c = log2(e)/T split as c32 + clo with clo > 0):
+//   element term    e = exp2(fma(l, clo, fma(l, c32, -off_c))), off_c = m_c*c32
+//                   in fp32, m_c the chunk max; summed per thread in fp32 and
+//                   across threads in fp64, published as fp32.
+//   chunk merge     S = sum_c s_c * exp2(off_c - M*c) in fp64, in chunk order.
+//   gathered p(x)   exp2((l_x - M)*c) / S in fp64; acceptance u*q(x) < p(x)
+//                   in fp64.
+//   final draw      chunk masses in fp64, sequential prefix over chunks, then a
+//                   fp64 block scan over the chosen chunk in token order.
+
+#include <hip/hip_runtime.h>
+#include <float.h>
+#include <stdint.h>
+
+#include "specverify.h"
+
+namespace sv {
+
+constexpr int WG = 256;
+constexpr int NWAVE = WG / 64;
+constexpr int CHUNK = 8192;
+constexpr int EPT = CHUNK / WG;   // elements per thread per chunk
+constexpr int MAX_NC = 512;       // chunks per row (vocab <= 4,194,304)
+constexpr int MAX_K = 63;         // k+1 positions fit one wave
+constexpr int STAGE_MAX = 49152;  // bytes of LDS the finalizer may stage statistics in
+constexpr int SPIN_MAX = 1 << 18; // polls before a wait gives up
+constexpr float NEG_INF = -__builtin_inff();
+constexpr float POS_INF = __builtin_inff();
+constexpr double LOG2E = 1.4426950408889634;
+constexpr uint32_t TAG = 0x80000000u;     // "fresh" bit of a hand-off word (high half)
+constexpr uint32_t F_NONE = 0x40000000u;  // helper decision: no residual to compute
+constexpr uint32_t F_BAD = 0x20000000u;   // residual chunk saw an invalid probability
+
+typedef unsigned long long u64;
+
+// Residual hand-off of one request (plain data).  Every 32-bit value sits in
+// the low half of a 64-bit word, so no word of the workspace ever has its top
+// ("fresh") bit set unless it is a hand-off word in flight.
+struct Setup {
+  double Sp, Sq;
+  float Mp, Mq;
+  int a;
+};
+struct alignas(16) SetupWords {
+  u64 w[8];   // Sp lo/hi, Sq lo/hi, Mp, Mq, a, (unused)
+};
+
+struct Params {
+  const void* target;
+  const void* draft;
+  const int32_t* kind;
+  const int32_t* cu;
+  const int32_t* drafts;
+  const float* u;
+  const float* temp;
+  const int32_t* top_k;
+  const float* top_p;
+  int32_t* accepted;
+  int32_t* out;
+  float* p_at;
+  float* q_at;
+  int32_t* status;
+  u64* cst;       // [rows][nc][2]  target chunk max / (sum or argmax)
+  u64* dst;       // [draft rows][nc][2]
+  u64* rx;        // [rows][3]      values at the draft id: l_x, e_x, draft l_x or q(x)
+  SetupWords* setup;  // [batch]
+  u64* dec;       // [batch][nc][2] helper decisions (target / draft chunk max of row a)
+  u64* res;       // [batch][nc]    residual mass per chunk
+  u64* thr_t;     // NULL when no request filters; float bits in the low half
+  u64* thr_d;
+  int64_t ld_t, ld_d;
+  int batch, total_rows, max_k, vocab, nc;
+  int S;          // chunks per producer strip
+  int ns;         // strips per row
+  int H;          // helper workgroups per request (nc, or 0 for the greedy entry)
+  int greedy_entry;
+};
+
+// ---------------------------------------------------------------------------
+// element access
+// ---------------------------------------------------------------------------
+template <typename T> struct VT;
+template <> struct VT<float> { static constexpr int VEC = 4; };
+template <> struct VT<uint16_t> { static constexpr int VEC = 8; };
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+__device__ __forceinline__ float fmax3nan(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);   // NaN-propagating
+}
+
+// A thread's share of one chunk, kept as the raw 128-bit words it was loaded
+// in (EPT elements); elements are unpacked when they are used.
+template <typename T>
+struct Seg {
+  static constexpr int VEC = VT<T>::VEC;
+  static constexpr int NV = EPT / VEC;
+  uint4 q[NV];
+  __device__ __forceinline__ float at(int i) const;
+};
+__device__ __forceinline__ uint32_t word_of(const uint4& w, int h) {
+  return h == 0 ? w.x : h == 1 ? w.y : h == 2 ? w.z : w.w;
+}
+template <> __device__ __forceinline__ float Seg<float>::at(int i) const {
+  return __uint_as_float(word_of(q[i / 4], i % 4));
+}
+template <> __device__ __forceinline__ float Seg<uint16_t>::at(int i) const {
+  const uint32_t u = word_of(q[i / 8], (i % 8) / 2);
+  return __uint_as_float((i & 1) ? (u & 0xffff0000u) : (u << 16));
+}
+
+// 32-bit pattern of `fill` in the element type (bf16: the upper half of f32)
+template <typename T> __device__ __forceinline__ uint32_t fill_bits(float f);
+template <> __device__ __forceinline__ uint32_t fill_bits<float>(float f) { return __float_as_uint(f); }
+template <> __device__ __forceinline__ uint32_t fill_bits<uint16_t>(float f) { return __float_as_uint(f) >> 16; }
+
+__device__ __forceinline__ uint32_t raw_bits(float x) { return __float_as_uint(x); }
+__device__ __forceinline__ uint32_t raw_bits(uint16_t x) { return (uint32_t)x; }
+
+// Elements [nv, VEC) of a loaded word replaced by the fill pattern.
+template <typename T>
+__device__ __forceinline__ uint4 mask_tail(uint4 w, int nv, uint32_t fb) {
+  constexpr int VEC = VT<T>::VEC;
+  uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (VEC == 4) {
+      d[k] = (k < nv) ? d[k] : fb;
+    } else {
+      const uint32_t lo = (2 * k < nv) ? (d[k] & 0xffffu) : fb;
+      const uint32_t hi = (2 * k + 1 < nv) ? (d[k] >> 16) : fb;
+      d[k] = lo | (hi << 16);
+    }
+  }
+  return make_uint4(d[0], d[1], d[2], d[3]);
+}
+
+// One 128-bit word of elements [off, off + VEC) of the chunk at cp, element
+// loads with `fill` from element n on (tensors whose rows are not 16-byte
+// aligned).
+template <typename T>
+__device__ __forceinline__ uint4 load_word_scalar(const T* __restrict__ cp, int off, int n,
+                                                  float fill) {
+  constexpr int VEC = VT<T>::VEC;
+  const uint32_t fb = fill_bits<T>(fill);
+  uint32_t e[VEC];
+#pragma unroll
+  for (int l = 0; l < VEC; ++l) e[l] = (off + l < n) ? raw_bits(cp[off + l]) : fb;
+  uint4 w;
+  if (VEC == 4) {
+    w.x = e[0]; w.y = e[1]; w.z = e[2]; w.w = e[3];
+  } else {
+    w.x = e[0] | (e[1 % VEC] << 16); w.y = e[2 % VEC] | (e[3 % VEC] << 16);
+    w.z = e[4 % VEC] | (e[5 % VEC] << 16); w.w = e[6 % VEC] | (e[7 % VEC] << 16);
+  }
+  return w;
+}
+
+// Fill the thread's words, word i at element offset offs(i) of the chunk at cp
+// (n valid elements).  al: the tensor's base address and row pitch are
+// multiples of 16 bytes, so every word is one 128-bit load issued from an
+// offset clamped to the last word that starts inside the row (always inside the
+// row's pitch); finish_words then masks the tail past n.  issue_words returns
+// without waiting for the data, so a chunk's loads can be in flight while the
+// previous chunk is reduced.
+template <typename T, typename OF>
+__device__ __forceinline__ void issue_words(const T* __restrict__ cp, int n, bool al, float fill,
+                                            OF offs, Seg<T>& s) {
+  constexpr int VEC = VT<T>::VEC;
+  if (al) {
+    const int last = ((n - 1) / VEC) * VEC;
+#pragma unroll
+    for (int i = 0; i < Seg<T>::NV; ++i)
+      s.q[i] = *reinterpret_cast<const uint4*>(cp + min(offs(i), last));
+  } else {
+#pragma unroll
+    for (int i = 0; i < Seg<T>::NV; ++i) s.q[i] = load_word_scalar<T>(cp, offs(i), n, fill);
+  }
+}
+
+template <typename T, typename OF>
+__device__ __forceinline__ void finish_words(int n, bool al, float fill, OF offs, Seg<T>& s) {
+  if (al && n < CHUNK) {   // uniform: only the last chunk of a row is partial
+    const uint32_t fb = fill_bits<T>(fill);
+#pragma unroll
+    for (int i = 0; i < Seg<T>::NV; ++i) s.q[i] = mask_tail<T>(s.q[i], n - offs(i), fb);
+  }
+}
+
+template <typename T, typename OF>
+__device__ __forceinline__ void load_words(const T* __restrict__ cp, int n, bool al, float fill,
+                                           OF offs, Seg<T>& s) {
+  issue_words<T>(cp, n, al, fill, offs, s);
+  finish_words<T>(n, al, fill, offs, s);
+}
+
+template <typename T>
+__device__ __forceinline__ int strided_off(int i) {
+  return (i * WG + (int)threadIdx.x) * VT<T>::VEC;
+}
+
+// element index in the chunk of the thread's slot (word slot / VEC, lane slot % VEC)
+template <typename T>
+__device__ __forceinline__ int strided_index(int slot) {
+  constexpr int VEC = VT<T>::VEC;
+  return strided_off<T>(slot / VEC) + slot % VEC;
+}
+
+// Contiguous layout: thread tid holds elements [tid*EPT, tid*EPT + EPT) in
+// token order (used by the final draws, which scan in token order).
+template <typename T>
+__device__ __forceinline__ void load_contig(const T* __restrict__ cp, int n, bool al, float fill,
+                                            Seg<T>& s) {
+  constexpr int VEC = VT<T>::VEC;
+  load_words<T>(cp, n, al, fill, [](int i) { return (int)threadIdx.x * EPT + i * VEC; }, s);
+}
+
+// ---------------------------------------------------------------------------
+// hand-off words (see the file comment)
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ void st_agent(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_agent(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void put_w(u64* w, uint32_t flags, uint32_t payload) {
+  st_agent(w, ((u64)(TAG | flags) << 32) | (u64)payload);
+}
+__device__ __forceinline__ uint32_t hi32(u64 v) { return (uint32_t)(v >> 32); }
+__device__ __forceinline__ uint32_t lo32(u64 v) { return (uint32_t)v; }
+
+// Wait for the tag of *w, consume the word (store it back untagged, payload
+// kept) and return it; returns 0 (no tag) when the wait runs out.
+__device__ __forceinline__ u64 take_w(u64* w) {
+  for (int it = 0; it < SPIN_MAX; ++it) {
+    const u64 v = ld_agent(w);
+    if (hi32(v) & TAG) {
+      st_agent(w, v & ((u64)(~TAG) << 32 | 0xffffffffull));
+      return v;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return 0ull;
+}
+
+// Make this thread's earlier agent-scope stores complete before the ones that
+// follow (used once per request, before its helpers' decision words).
+__device__ __forceinline__ void stores_complete() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// ---------------------------------------------------------------------------
+// block reductions (fixed order: deterministic)
+// ---------------------------------------------------------------------------
+struct Smem {
+  float f[NWAVE];
+  double d[NWAVE];
+  int i[NWAVE];
+  unsigned long long u[NWAVE];
+};
+
+__device__ __forceinline__ float block_max(float x, Smem& sm) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmax3nan(x, __shfl_xor(x, o, 64));
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sm.f[w] = x;
+  __syncthreads();
+  float r = sm.f[0];
+#pragma unroll
+  for (int k = 1; k < NWAVE; ++k) r = fmax3nan(r, sm.f[k]);
+  return r;
+}
+
+__device__ __forceinline__ int block_min_i(int x, Smem& sm) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o, 64));
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sm.i[w] = x;
+  __syncthreads();
+  int r = sm.i[0];
+#pragma unroll
+  for (int k = 1; k < NWAVE; ++k) r = min(r, sm.i[k]);
+  return r;
+}
+
+__device__ __forceinline__ int block_max_i(int x, Smem& sm) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o, 64));
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sm.i[w] = x;
+  __syncthreads();
+  int r = sm.i[0];
+#pragma unroll
+  for (int k = 1; k < NWAVE; ++k) r = max(r, sm.i[k]);
+  return r;
+}
+
+__device__ __forceinline__ double block_sum_d(double x, Smem& sm) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sm.d[w] = x;
+  __syncthreads();
+  double r = sm.d[0];
+#pragma unroll
+  for (int k = 1; k < NWAVE; ++k) r += sm.d[k];
+  return r;
+}
+
+// Inclusive fp64 scan over the block in thread order; also returns the
+// exclusive value (the inclusive value of the previous thread).
+__device__ __forceinline__ void block_scan_d(double own, double& excl, double& incl, Smem& sm) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  double x = own;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) sm.d[w] = x;
+  __syncthreads();
+  double carry = 0.0;
+  for (int k = 0; k < w; ++k) carry += sm.d[k];
+  x += carry;
+  const double prev = __shfl_up(x, 1, 64);
+  incl = x;
+  excl = (lane == 0) ? carry : prev;
+}
+
+// ---------------------------------------------------------------------------
+// per-request parameters
+// ---------------------------------------------------------------------------
+struct Req {
+  float T;
+  bool greedy;
+  int kind;
+  bool bad_param;
+  int K;
+  float P;
+  bool filt;
+  double ce;  // c32 + clo, the multiplier the element terms use
+  float c32, clo;
+};
+
+__device__ __forceinline__ Req load_req(const Params& P, int b) {
+  Req R;
+  R.T = P.greedy_entry ? 0.f : P.temp[b];
+  R.greedy = P.greedy_entry || !(R.T >= FLT_MIN);
+  R.kind = R.greedy ? -1 : P.kind[b];
+  R.bad_param = !R.greedy &&
+                (R.T == POS_INF || R.kind < SV_DRAFT_ONEHOT || R.kind > SV_DRAFT_PROBS ||
+                 (R.kind != SV_DRAFT_ONEHOT && P.draft == nullptr));
+  R.K = (!R.greedy && P.top_k) ? P.top_k[b] : 0;
+  R.P = (!R.greedy && P.top_p) ? P.top_p[b] : 1.f;
+  if (R.K >= P.vocab) R.K = 0;
+  R.filt = R.K > 0 || (R.P > 0.f && R.P < 1.f);
+  if (!R.greedy && !R.bad_param) {
+    const double ce = LOG2E / (double)R.T;
+    const float c32 = __double2float_rd(ce);
+    float clo = (float)(ce - (double)c32);
+    clo = fmaxf(clo, FLT_MIN);   // strictly positive: -inf * clo stays -inf
+    R.c32 = c32;
+    R.clo = clo;
+    R.ce = (double)c32 + (double)clo;
+  } else {
+    R.c32 = 0.f; R.clo = 0.f; R.ce = 0.0;
+  }
+  return R;
+}
+
+__device__ __forceinline__ bool req_valid(const Params& P, int b, int cu0, int cu1, int k) {
+  return cu0 >= 0 && cu1 <= P.total_rows && k >= 0 && k <= P.max_k && cu0 - b >= 0 &&
+         cu0 - b + k <= P.total_rows - P.batch;
+}
+
+__device__ __forceinline__ float thr_of(const u64* t, int i) {
+  return __uint_as_float((uint32_t)t[i]);
+}
+
+__device__ __forceinline__ float chunk_off(float m, float c32) { return m * c32; }
+
+__device__ __forceinline__ float eterm(float v, float c32, float clo, float off) {
+  return __builtin_amdgcn_exp2f(__builtin_fmaf(v, clo, __builtin_fmaf(v, c32, -off)));
+}
+
+// ---------------------------------------------------------------------------
+// producers: statistics of one chunk of one row
+// ---------------------------------------------------------------------------
+struct CStat {
+  float m;     // chunk max (NaN / +inf propagate)
+  float s;     // sum of element terms relative to m (sampled rows)
+  float sx;    // the same sum without the element xl (when asked for)
+  int arg;     // lowest index of the max within the chunk (greedy rows)
+};
+
+// Statistics of one chunk held in the strided layout.  VF(i) gives the value
+// of slot i (masked to -inf below a top-k/top-p threshold when there is one).
+// xl: chunk-local index of the draft id, or -1.
+template <typename T, typename VF>
+__device__ __forceinline__ CStat chunk_stats_v(VF val, bool greedy, float c32, float clo, int xl,
+                                               Smem& sm) {
+  float m = NEG_INF;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) m = fmax3nan(m, val(i));
+  const float M = block_max(m, sm);
+  CStat st;
+  st.m = M;
+  st.s = 0.f;
+  st.sx = 0.f;
+  st.arg = INT32_MAX;
+  if (greedy) {
+    int cand = INT32_MAX;
+    if (m == M) {   // only the threads that hold the chunk max search for its first slot
+      int slot = EPT;
+#pragma unroll
+      for (int i = EPT - 1; i >= 0; --i) slot = (val(i) == M) ? i : slot;
+      cand = strided_index<T>(slot);
+    }
+    st.arg = block_min_i(cand, sm);
+  } else if (M > NEG_INF && M < POS_INF) {
+    const float off = chunk_off(M, c32);
+    float acc = 0.f;
+    if (xl < 0) {
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) acc += eterm(val(i), c32, clo, off);
+      st.s = (float)block_sum_d((double)acc, sm);
+    } else {
+      // the thread that holds element xl also sums its terms without it
+      constexpr int VEC = VT<T>::VEC;
+      const int owner = (xl / VEC) % WG;
+      const int xslot = ((xl / VEC) / WG) * VEC + xl % VEC;
+      const int ix = ((int)threadIdx.x == owner) ? xslot : -1;
+      float accx = 0.f;
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) {
+        const float e = eterm(val(i), c32, clo, off);
+        acc += e;
+        accx += (i == ix) ? 0.f : e;
+      }
+      st.s = (float)block_sum_d((double)acc, sm);
+      st.sx = (float)block_sum_d((double)accx, sm);
+    }
+  }
+  return st;
+}
+
+// Mask, in place, every element below tau (a top-k / top-p threshold) to -inf.
+// NaN compares false and is kept, so the fault is still seen.
+__device__ __forceinline__ uint32_t mask16(uint32_t h, float tau) {
+  return (__uint_as_float(h << 16) < tau) ? 0xff80u : h;
+}
+template <typename T> __device__ __forceinline__ void apply_tau(Seg<T>& sg, float tau);
+template <> __device__ __forceinline__ void apply_tau<float>(Seg<float>& sg, float tau) {
+#pragma unroll
+  for (int i = 0; i < Seg<float>::NV; ++i) {
+    uint32_t d[4] = {sg.q[i].x, sg.q[i].y, sg.q[i].z, sg.q[i].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) d[k] = (__uint_as_float(d[k]) < tau) ? 0xff800000u : d[k];
+    sg.q[i] = make_uint4(d[0], d[1], d[2], d[3]);
+  }
+}
+template <> __device__ __forceinline__ void apply_tau<uint16_t>(Seg<uint16_t>& sg, float tau) {
+#pragma unroll
+  for (int i = 0; i < Seg<uint16_t>::NV; ++i) {
+    uint32_t d[4] = {sg.q[i].x, sg.q[i].y, sg.q[i].z, sg.q[i].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) d[k] = mask16(d[k] & 0xffffu, tau) | (mask16(d[k] >> 16, tau) << 16);
+    sg.q[i] = make_uint4(d[0], d[1], d[2], d[3]);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ CStat chunk_stats(Seg<T>& sg, bool greedy, float tau, float c32,
+                                             float clo, int xl, Smem& sm) {
+  if (tau > NEG_INF) apply_tau<T>(sg, tau);
+  auto val = [&](int i) { return sg.at(i); };
+  return chunk_stats_v<T>(val, greedy, c32, clo, xl, sm);
+}
+
+__device__ __forceinline__ void publish_stat(u64* w, const CStat& st, bool greedy) {
+  put_w(w, 0u, __float_as_uint(st.m));
+  put_w(w + 1, 0u, greedy ? (uint32_t)st.arg : __float_as_uint(st.s));
+}
+
+// chunks per producer strip (64 KiB of bf16 or fp32 target data)
+template <typename TT> struct Strip;
+template <> struct Strip<uint16_t> { static constexpr int S = 4; };
+template <> struct Strip<float> { static constexpr int S = 2; };
+
+// Words of one chunk of either element type (sized for the wider one).
+template <typename TT, typename TD>
+struct Buf {
+  static constexpr int NQ = Seg<TT>::NV > Seg<TD>::NV ? Seg<TT>::NV : Seg<TD>::NV;
+  uint4 q[NQ];
+};
+
+template <typename T, typename TT, typename TD>
+__device__ __forceinline__ void buf_issue(const T* __restrict__ cp, int n, bool al,
+                                          Buf<TT, TD>& b) {
+  Seg<T> sg;
+  issue_words<T>(cp, n, al, NEG_INF, [](int i) { return strided_off<T>(i); }, sg);
+#pragma unroll
+  for (int i = 0; i < Seg<T>::NV; ++i) b.q[i] = sg.q[i];
+}
+
+template <typename T, typename TT, typename TD>
+__device__ __forceinline__ CStat buf_stats(const Buf<TT, TD>& b, int n, bool al, bool greedy,
+                                           float tau, float c32, float clo, int xl, Smem& sm) {
+  Seg<T> sg;
+#pragma unroll
+  for (int i = 0; i < Seg<T>::NV; ++i) sg.q[i] = b.q[i];
+  finish_words<T>(n, al, NEG_INF, [](int i) { return strided_off<T>(i); }, sg);
+  return chunk_stats<T>(sg, greedy, tau, c32, clo, xl, sm);
+}
+
+// Producer of request b, row j, strip s: statistics of S chunks of the target
+// row (and of the draft row for draft-logit requests).  The chunks are a
+// two-deep pipeline of tasks (target chunk, then draft chunk when there is one):
+// task i+1's loads are issued before task i is reduced.
+template <typename TT, typename TD, bool AL>
+__device__ __forceinline__ void produce(const Params& P, const Req& R, int b, int cu0, int k,
+                                        int j, int s, Smem& sm) {
+  constexpr int S = Strip<TT>::S;
+  const int nc = P.nc;
+  const int row = cu0 + j;
+  const int d0 = cu0 - b;
+  const TT* trow = (const TT*)P.target + (int64_t)row * P.ld_t;
+  const float tau = (P.thr_t && R.filt) ? thr_of(P.thr_t, row) : NEG_INF;
+  const bool has_d = R.kind == SV_DRAFT_LOGITS && j < k;
+  const TD* drow = (const TD*)P.draft + (int64_t)(d0 + j) * P.ld_d;
+  const float taud = (has_d && P.thr_d && R.filt) ? thr_of(P.thr_d, d0 + j) : NEG_INF;
+  const int x = (!R.greedy && j < k) ? P.drafts[d0 + j] : -1;
+  const int c_begin = s * S;
+  const int c_end = min(c_begin + S, nc);
+  const int per = has_d ? 2 : 1;
+  const int nt = (c_end - c_begin) * per;
+
+  Buf<TT, TD> cur, nxt;
+  buf_issue<TT>(trow + c_begin * CHUNK, min(CHUNK, P.vocab - c_begin * CHUNK), AL, cur);
+  for (int t = 0; t < nt; ++t) {
+    const int c = c_begin + t / per;
+    const bool is_d = has_d && (t & 1);
+    const int c0 = c * CHUNK;
+    const int n = min(CHUNK, P.vocab - c0);
+    if (t + 1 < nt) {   // next task's loads go out before this one is reduced
+      const int cn = c_begin + (t + 1) / per;
+      const int nn = min(CHUNK, P.vocab - cn * CHUNK);
+      if (has_d && ((t + 1) & 1)) buf_issue<TD>(drow + cn * CHUNK, nn, AL, nxt);
+      else buf_issue<TT>(trow + cn * CHUNK, nn, AL, nxt);
+    }
+    const bool xin = x >= c0 && x < c0 + n;
+    if (!is_d) {
+      const CStat st = buf_stats<TT>(cur, n, AL, R.greedy, tau, R.c32, R.clo,
+                                     xin ? x - c0 : -1, sm);
+      if (threadIdx.x == 0) {
+        publish_stat(P.cst + ((int64_t)row * nc + c) * 2, st, R.greedy);
+        if (xin) {
+          float lx = to_f(trow[x]);
+          if (lx < tau) lx = NEG_INF;
+          put_w(P.rx + (int64_t)row * 3 + 0, 0u, __float_as_uint(lx));
+          put_w(P.rx + (int64_t)row * 3 + 1, 0u, __float_as_uint(st.sx));
+        }
+        if (R.kind == SV_DRAFT_PROBS && j < k && xin)
+          put_w(P.rx + (int64_t)row * 3 + 2, 0u, __float_as_uint(to_f(drow[x])));
+      }
+    } else {
+      const CStat sd = buf_stats<TD>(cur, n, AL, false, taud, R.c32, R.clo, -1, sm);
+      if (threadIdx.x == 0) {
+        publish_stat(P.dst + ((int64_t)(d0 + j) * nc + c) * 2, sd, false);
+        if (xin) {
+          float dlx = to_f(drow[x]);
+          if (dlx < taud) dlx = NEG_INF;
+          put_w(P.rx + (int64_t)row * 3 + 2, 0u, __float_as_uint(dlx));
+        }
+      }
+    }
+    cur = nxt;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// final draw over one chunk in token order
+// ---------------------------------------------------------------------------
+struct DrawShared {
+  double E[MAX_NC];
+  double tl;
+  double wexcl;
+  int chunk;
+  int tok;
+  int win;
+  int wlast;
+};
+
+// Inverse CDF inside one chunk [c0, c0+n) of a row, in token order.  Thread
+// tid owns the segment [c0 + tid*EPT, c0 + tid*EPT + EPT).  weight(a, b, e)
+// gives the fp64 weight of element e from its values a (row A) and b (row B,
+// only when TWO); it is evaluated again, on the same inputs, when the
+// segment that holds the target is searched.  Returns the first element whose
+// running sum exceeds tl (the last positive element when rounding leaves
+// none).
+template <typename TA, typename TB, bool TWO, typename WF>
+__device__ __forceinline__ int draw_chunk(const TA* __restrict__ pa, const TB* __restrict__ pb, bool avec,
+                          bool bvec, float bfill, int c0, int n, double tl, WF weight, Smem& sm,
+                          DrawShared& ds) {
+  const int tid = threadIdx.x;
+  const int seg = tid * EPT;               // offset of this thread's segment in the chunk
+  double own = 0.0;
+  int last_pos = -1;
+  {
+    Seg<TA> sa;
+    Seg<TB> sb;
+    load_contig<TA>(pa + c0, n, avec, NEG_INF, sa);
+    if (TWO) load_contig<TB>(pb + c0, n, bvec, bfill, sb);
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const double w = weight(sa.at(i), TWO ? sb.at(i) : 0.f, c0 + seg + i);
+      own += w;
+      last_pos = (w > 0.0) ? c0 + seg + i : last_pos;
+      if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound live fp64 temporaries
+    }
+  }
+  double excl, incl;
+  block_scan_d(own, excl, incl, sm);
+  if (tid == 0) ds.win = -1;
+  __syncthreads();
+  if (excl <= tl && tl < incl) {     // at most one thread: the intervals are disjoint
+    ds.win = tid;
+    ds.wexcl = excl;
+    ds.wlast = last_pos;
+  }
+  __syncthreads();
+  const int win = ds.win;
+  if (win < 0) return block_max_i(last_pos, sm);   // tl at or past the chunk total
+  if (tid < 64) {
+    const int l = tid;
+    const int off = win * EPT + l;
+    const bool ok = l < EPT && off < n;
+    const float a = ok ? to_f(pa[c0 + off]) : NEG_INF;
+    const float bv = (ok && TWO) ? to_f(pb[c0 + off]) : bfill;
+    const double w = ok ? weight(a, bv, c0 + off) : 0.0;
+    double x = w;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const double y = __shfl_up(x, o, 64);
+      if (l >= o) x += y;
+    }
+    const uint64_t hit = __ballot(w > 0.0 && ds.wexcl + x > tl);
+    if (l == 0) ds.tok = hit ? c0 + win * EPT + (int)__builtin_ctzll(hit) : ds.wlast;
+  }
+  __syncthreads();
+  return ds.tok;
+}
+
+// Pick the chunk holding target = u*W given chunk masses in ds.E[0..nc).
+// Returns false when W == 0.  Thread 0 computes; result in ds.chunk, ds.tl.
+__device__ __forceinline__ bool pick_chunk(int nc, double u, DrawShared& ds) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double W = 0.0;
+    for (int c = 0; c < nc; ++c) W += ds.E[c];
+    int ch = -1;
+    double tl = 0.0;
+    if (W > 0.0) {
+      const double target = u * W;
+      double pre = 0.0;
+      int last = -1;
+      for (int c = 0; c < nc; ++c) {
+        if (ds.E[c] > 0.0) last = c;
+        const double nxt = pre + ds.E[c];
+        if (nxt > target && ds.E[c] > 0.0) {
+          ch = c;
+          tl = target - pre;
+          break;
+        }
+        pre = nxt;
+      }
+      if (ch < 0) {   // rounding: target at or past the total
+        ch = last;
+        tl = POS_INF;
+      }
+    }
+    ds.chunk = ch;
+    ds.tl = tl;
+  }
+  __syncthreads();
+  return ds.chunk >= 0;
+}
+
+
+// Draw from p of one target row (bonus draw, one-hot rejection with
+// `exclude` = the rejected draft id, zero-residual fallback).  cm(c) and
+// cs(c) give chunk c's max and sum of terms (cs_x: the sum of x's chunk
+// without x); M is the merged row max.  Returns the token (all threads).
+template <typename TT, bool AL, typename FM, typename FS>
+__device__ __forceinline__ int draw_target_row(const Params& P, const Req& R, int row, float M, int exclude,
+                               float csx, float tau, double u, FM cm, FS cs, Smem& sm,
+                               DrawShared& ds) {
+  const int nc = P.nc;
+  const double Mc = (double)M * R.ce;
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    for (int c = threadIdx.x; c < nc; c += WG) {
+      const float m = cm(c);
+      double e = 0.0;
+      if (m > NEG_INF) {
+        const double R_c = exp2((double)chunk_off(m, R.c32) - Mc);
+        const float sc = (exclude >= 0 && exclude / CHUNK == c) ? csx : cs(c);
+        e = (double)sc * R_c;
+        if (!(e > 0.0)) e = 0.0;
+      }
+      ds.E[c] = e;
+    }
+    if (pick_chunk(nc, u, ds)) break;
+    if (exclude < 0) return -1;
+    exclude = -1;   // only the rejected token had mass: fall back to p itself
+  }
+  const int ch = ds.chunk;
+  const float m = cm(ch);
+  const double R_c = exp2((double)chunk_off(m, R.c32) - Mc);
+  const double tl = ds.tl / R_c;
+  const float off = chunk_off(m, R.c32);
+  const int c0 = ch * CHUNK;
+  const int n = min(CHUNK, P.vocab - c0);
+  const TT* rp = (const TT*)P.target + (int64_t)row * P.ld_t;
+  const bool vec_ok = AL;
+  const float c32 = R.c32, clo = R.clo;
+  auto wf = [=](float x, float, int e) -> double {
+    if (x < tau || e == exclude) x = NEG_INF;
+    return (double)eterm(x, c32, clo, off);
+  };
+  return draw_chunk<TT, TT, false>(rp, rp, vec_ok, vec_ok, 0.f, c0, n, tl, wf, sm, ds);
+}
+
+__device__ __forceinline__ void write_fault(const Params& P, int b, int cu0, int k, int code) {
+  for (int j = threadIdx.x; j <= k; j += WG) P.out[cu0 + j] = -1;
+  const int d0 = cu0 - b;
+  for (int j = threadIdx.x; j < k; j += WG) {
+    if (P.p_at) P.p_at[d0 + j] = __builtin_nanf("");
+    if (P.q_at) P.q_at[d0 + j] = __builtin_nanf("");
+  }
+  if (threadIdx.x == 0) {
+    P.accepted[b] = -1;
+    P.status[b] = code;
+  }
+}
+
+// Helpers of a request wait for decision words exactly when this holds.
+__device__ __forceinline__ bool has_helpers(const Params& P, const Req& R) {
+  return P.H > 0 && !R.greedy && !R.bad_param &&
+         (R.kind == SV_DRAFT_LOGITS || R.kind == SV_DRAFT_PROBS);
+}
+
+__device__ __forceinline__ void helpers_none(const Params& P, int b) {
+  for (int c = threadIdx.x; c < P.nc; c += WG)
+    put_w(P.dec + ((int64_t)b * P.nc + c) * 2, F_NONE, 0u);
+}
+
+// ---------------------------------------------------------------------------
+// finalizer: merge a request's statistics, scan, outputs, draws
+// ---------------------------------------------------------------------------
+struct FinShared {
+  float M[64], Mq[64];
+  double S[64], Sq[64];
+  float lx[64], sx[64], dlx[64];
+  int x[64];
+  int a, code, mode, timeout;
+};
+
+template <typename TT, typename TD, bool AL>
+__device__ __forceinline__ void finalize(const Params& P, int b, int cu0, int k, const Req& R, Smem& sm,
+                         FinShared& fs, DrawShared& ds, uint32_t* stage) {
+  const int nc = P.nc;
+  const int d0 = cu0 - b;
+  const int tid = threadIdx.x;
+  const bool logits = R.kind == SV_DRAFT_LOGITS;
+  const bool sampled = !R.greedy;
+  // staged statistics: m and s (or argmax) of target rows 0..k (slots 0..k) and
+  // draft rows 0..k-1 (slots k+1..2k), chunk-major within a row
+  float* st_m = reinterpret_cast<float*>(stage);
+  uint32_t* st_s = stage + (size_t)(2 * P.max_k + 1) * nc;
+
+  if (tid == 0) fs.timeout = 0;
+  if (tid < 64) fs.x[tid] = (tid < k) ? P.drafts[d0 + tid] : -1;
+  __syncthreads();
+  bool badtok_any = false;
+  for (int i = 0; i < k; ++i) badtok_any |= (fs.x[i] < 0 || fs.x[i] >= P.vocab);
+
+  if (!R.bad_param) {
+    // wait for, stage and consume every word the request's producers published
+    // (also when a draft id is out of range: the statistics were still written)
+    const int nA = (k + 1) * nc * 2;
+    const int nB = logits ? k * nc * 2 : 0;
+    const int rxw = sampled ? ((R.kind == SV_DRAFT_ONEHOT) ? 2 : 3) : 0;
+    const int nC = k * rxw;
+    int to = 0;
+    for (int w = tid; w < nA + nB + nC; w += WG) {
+      u64* src;
+      int slot = -1, c = 0, f = 0, jr = 0;
+      if (w < nA) {
+        jr = w / (2 * nc);
+        c = (w / 2) % nc;
+        f = w & 1;
+        slot = jr;
+        src = P.cst + ((int64_t)(cu0 + jr) * nc + c) * 2 + f;
+      } else if (w < nA + nB) {
+        const int w2 = w - nA;
+        jr = w2 / (2 * nc);
+        c = (w2 / 2) % nc;
+        f = w2 & 1;
+        slot = k + 1 + jr;
+        src = P.dst + ((int64_t)(d0 + jr) * nc + c) * 2 + f;
+      } else {
+        const int w3 = w - nA - nB;
+        jr = w3 / rxw;
+        f = w3 % rxw;
+        if (fs.x[jr] < 0 || fs.x[jr] >= P.vocab) continue;   // never written
+        src = P.rx + (int64_t)(cu0 + jr) * 3 + f;
+      }
+      const u64 v = take_w(src);
+      if (!(hi32(v) & TAG)) to = 1;
+      const uint32_t pay = lo32(v);
+      if (slot >= 0) {
+        if (f == 0) st_m[slot * nc + c] = __uint_as_float(pay);
+        else st_s[slot * nc + c] = pay;
+      } else if (f == 0) {
+        fs.lx[jr] = __uint_as_float(pay);
+      } else if (f == 1) {
+        fs.sx[jr] = __uint_as_float(pay);
+      } else {
+        fs.dlx[jr] = __uint_as_float(pay);
+      }
+    }
+    if (to) atomicOr(&fs.timeout, 1);
+  }
+  __syncthreads();
+
+  if (tid < 64) {
+    const int j = tid;
+    bool nonfin = false, empty = false, acc = false;
+    float M = NEG_INF, Mq = NEG_INF;
+    double S = 0.0, Sq = 0.0;
+    int g = -1;
+    const bool staged = !R.bad_param && !badtok_any && !fs.timeout;
+    if (j <= k && staged) {
+      const float* mrow = st_m + j * nc;
+      const uint32_t* srow = st_s + j * nc;
+      for (int c = 0; c < nc; ++c) M = fmax3nan(M, mrow[c]);
+      if (R.greedy) {
+        for (int c = 0; c < nc; ++c) {
+          if (mrow[c] == M) {
+            g = c * CHUNK + (int)srow[c];
+            break;
+          }
+        }
+      } else if (M > NEG_INF && M < POS_INF) {
+        const double Mc = (double)M * R.ce;
+        for (int c = 0; c < nc; ++c)
+          if (mrow[c] > NEG_INF)
+            S += (double)__uint_as_float(srow[c]) * exp2((double)chunk_off(mrow[c], R.c32) - Mc);
+      }
+      nonfin = (M != M) || M == POS_INF;
+      empty = M == NEG_INF;
+      if (logits && j < k) {
+        const float* qm = st_m + (k + 1 + j) * nc;
+        const uint32_t* qs = st_s + (k + 1 + j) * nc;
+        for (int c = 0; c < nc; ++c) Mq = fmax3nan(Mq, qm[c]);
+        if (Mq > NEG_INF && Mq < POS_INF) {
+          const double Mc = (double)Mq * R.ce;
+          for (int c = 0; c < nc; ++c)
+            if (qm[c] > NEG_INF)
+              Sq += (double)__uint_as_float(qs[c]) * exp2((double)chunk_off(qm[c], R.c32) - Mc);
+        }
+        nonfin = nonfin || (Mq != Mq) || Mq == POS_INF;
+        empty = empty || Mq == NEG_INF;
+      }
+    }
+    const int x = fs.x[j];
+    double px = 0.0, qx = 0.0;
+    const uint64_t m_pre = __ballot(nonfin || empty);
+    if (j < k && m_pre == 0 && staged) {
+      if (R.greedy) {
+        acc = (x == g);
+        px = acc ? 1.0 : 0.0;
+        qx = 1.0;
+      } else {
+        px = exp2(((double)fs.lx[j] - (double)M) * R.ce) / S;
+        if (logits) {
+          qx = exp2(((double)fs.dlx[j] - (double)Mq) * R.ce) / Sq;
+        } else if (R.kind == SV_DRAFT_PROBS) {
+          qx = (double)fs.dlx[j];
+          if (!(qx >= 0.0 && qx < (double)POS_INF)) nonfin = true;
+        } else {
+          qx = 1.0;
+        }
+        acc = (double)P.u[cu0 + j] * qx < px;
+      }
+    }
+    const uint64_t m_nf = __ballot(nonfin);
+    const uint64_t m_em = __ballot(empty);
+    const uint64_t m_acc = __ballot(acc && j < k);
+    int code = SV_ROW_OK;
+    if (R.bad_param) code = SV_ROW_BAD_PARAM;
+    else if (badtok_any) code = SV_ROW_BAD_TOKEN;
+    else if (fs.timeout) code = SV_ROW_INTERNAL;
+    else if (m_nf) code = SV_ROW_NONFINITE;
+    else if (m_em) code = SV_ROW_EMPTY;
+    int a = (int)__builtin_ctzll(~m_acc);
+    if (a > k) a = k;
+    fs.M[j] = M; fs.Mq[j] = Mq; fs.S[j] = S; fs.Sq[j] = Sq;
+    if (code == SV_ROW_OK) {
+      if (j < k) {
+        if (P.p_at) P.p_at[d0 + j] = (float)px;
+        if (P.q_at) P.q_at[d0 + j] = (float)qx;
+      }
+      if (j <= k) {
+        int tok = -1;
+        if (j < a) tok = x;
+        else if (j == a && R.greedy) tok = g;
+        if (j != a || R.greedy) P.out[cu0 + j] = tok;
+      }
+    }
+    if (j == 0) {
+      fs.code = code;
+      fs.a = a;
+      int mode = 0;   // 0 done, 1 draw from the target row here, 2 residual by the helpers
+      if (code == SV_ROW_OK && sampled)
+        mode = (a == k || R.kind == SV_DRAFT_ONEHOT) ? 1 : 2;
+      fs.mode = mode;
+    }
+  }
+  __syncthreads();
+  const int code = fs.code;
+  const int a = fs.a;
+  const int mode = fs.mode;
+  if (code != SV_ROW_OK) {
+    write_fault(P, b, cu0, k, code);
+    if (has_helpers(P, R)) helpers_none(P, b);
+    return;
+  }
+  if (mode == 1) {
+    const int row = cu0 + a;
+    const float tau = (P.thr_t && R.filt) ? thr_of(P.thr_t, row) : NEG_INF;
+    const int exclude = (a < k) ? fs.x[a] : -1;
+    const float* mrow = st_m + a * nc;
+    const uint32_t* srow = st_s + a * nc;
+    const int t = draw_target_row<TT, AL>(
+        P, R, row, fs.M[a], exclude, exclude >= 0 ? fs.sx[a] : 0.f, tau,
+        (double)P.u[cu0 + k], [=](int c) { return mrow[c]; },
+        [=](int c) { return __uint_as_float(srow[c]); }, sm, ds);
+    if (tid == 0) P.out[row] = t;
+    if (has_helpers(P, R)) helpers_none(P, b);
+  } else if (mode == 2) {
+    if (tid == 0) {
+      u64* su = P.setup[b].w;
+      const u64 sp = (u64)__double_as_longlong(fs.S[a]);
+      const u64 sq = (u64)__double_as_longlong(fs.Sq[a]);
+      st_agent(su + 0, sp & 0xffffffffull);
+      st_agent(su + 1, sp >> 32);
+      st_agent(su + 2, sq & 0xffffffffull);
+      st_agent(su + 3, sq >> 32);
+      st_agent(su + 4, (u64)__float_as_uint(fs.M[a]));
+      st_agent(su + 5, (u64)__float_as_uint(fs.Mq[a]));
+      st_agent(su + 6, (u64)(uint32_t)a);
+    }
+    // the setup is complete before any helper can see its decision word
+    if (tid == 0) stores_complete();
+    __syncthreads();
+    for (int c = tid; c < nc; c += WG) {
+      u64* dw = P.dec + ((int64_t)b * nc + c) * 2;
+      if (logits) put_w(dw + 1, 0u, __float_as_uint(st_m[(k + 1 + a) * nc + c]));
+      put_w(dw, 0u, __float_as_uint(st_m[a * nc + c]));
+    }
+  }
+  if (tid == 0) {
+    P.accepted[b] = a;
+    P.status[b] = SV_ROW_OK;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// helpers: residual max(0, p - q) at the first rejection
+// ---------------------------------------------------------------------------
+struct ResCtx {
+  float offp, offq;
+  double sp, sq;   // per-chunk scale R_c / S of target and draft
+  float taup, tauq;
+};
+
+// Residual weight of one token from its target value lp and draft value lq
+// (logit, or probability for a probability draft).
+template <bool LOGITS>
+__device__ __forceinline__ double resid_elem(float lp, float lq, const Req& R, const ResCtx& X) {
+  if (lp < X.taup) lp = NEG_INF;
+  const double p = (double)eterm(lp, R.c32, R.clo, X.offp) * X.sp;
+  double q;
+  if (LOGITS) {
+    if (lq < X.tauq) lq = NEG_INF;
+    q = (double)eterm(lq, R.c32, R.clo, X.offq) * X.sq;
+  } else {
+    q = (double)lq;
+  }
+  const double w = p - q;
+  return w > 0.0 ? w : 0.0;
+}
+
+__device__ __forceinline__ void res_ctx(const Params& P, const Req& R, const Setup& su, float mp,
+                                        float mq, int trow, int drow, ResCtx& X) {
+  X.offp = (mp > NEG_INF) ? chunk_off(mp, R.c32) : 0.f;
+  X.sp = (mp > NEG_INF) ? exp2((double)X.offp - (double)su.Mp * R.ce) / su.Sp : 0.0;
+  X.taup = (P.thr_t && R.filt) ? thr_of(P.thr_t, trow) : NEG_INF;
+  X.offq = 0.f;
+  X.sq = 0.0;
+  X.tauq = NEG_INF;
+  if (R.kind == SV_DRAFT_LOGITS) {
+    X.offq = (mq > NEG_INF) ? chunk_off(mq, R.c32) : 0.f;
+    X.sq = (mq > NEG_INF) ? exp2((double)X.offq - (double)su.Mq * R.ce) / su.Sq : 0.0;
+    X.tauq = (P.thr_d && R.filt) ? thr_of(P.thr_d, drow) : NEG_INF;
+  }
+}
+
+struct HelpShared {
+  float mp, mq;
+  int none, timeout, bad;
+};
+
+template <typename TT, typename TD, bool AL>
+__device__ __forceinline__ void helper(const Params& P, int b, int c, Smem& sm, DrawShared& ds, HelpShared& hs) {
+  const int nc = P.nc;
+  const int cu0 = P.cu[b];
+  const int cu1 = P.cu[b + 1];
+  const int k = cu1 - cu0 - 1;
+  if (!req_valid(P, b, cu0, cu1, k)) return;
+  const Req R = load_req(P, b);
+  if (!has_helpers(P, R)) return;
+  const bool logits = R.kind == SV_DRAFT_LOGITS;
+  if (threadIdx.x == 0) {
+    u64* dw = P.dec + ((int64_t)b * nc + c) * 2;
+    const u64 v = take_w(dw);
+    hs.timeout = !(hi32(v) & TAG);
+    hs.none = (hi32(v) & F_NONE) != 0;
+    hs.mp = __uint_as_float(lo32(v));
+    hs.mq = 0.f;
+    if (!hs.timeout && !hs.none && logits) {
+      const u64 vq = take_w(dw + 1);
+      if (!(hi32(vq) & TAG)) hs.timeout = 1;
+      hs.mq = __uint_as_float(lo32(vq));
+    }
+  }
+  __syncthreads();
+  if (hs.none) return;
+  const bool last = c == nc - 1;
+  if (hs.timeout) {
+    if (last) write_fault(P, b, cu0, k, SV_ROW_INTERNAL);
+    return;
+  }
+  Setup su;
+  {
+    const u64* sw = P.setup[b].w;
+    su.Sp = __longlong_as_double((long long)(ld_agent(sw + 0) | (ld_agent(sw + 1) << 32)));
+    su.Sq = __longlong_as_double((long long)(ld_agent(sw + 2) | (ld_agent(sw + 3) << 32)));
+    su.Mp = __uint_as_float((uint32_t)ld_agent(sw + 4));
+    su.Mq = __uint_as_float((uint32_t)ld_agent(sw + 5));
+    su.a = (int)(uint32_t)ld_agent(sw + 6);
+  }
+  const int a = su.a;
+  if (a < 0 || a >= k) {   // cannot happen after a fresh decision; never index with it
+    if (last) write_fault(P, b, cu0, k, SV_ROW_INTERNAL);
+    return;
+  }
+  const int trow = cu0 + a;
+  const int drow = cu0 - b + a;
+  const TT* tp = (const TT*)P.target + (int64_t)trow * P.ld_t;
+  const TD* dp = (const TD*)P.draft + (int64_t)drow * P.ld_d;
+  const bool tvec = AL;
+  const bool dvec = AL;
+  const bool probs = R.kind == SV_DRAFT_PROBS;
+  const float qfill = probs ? 0.f : NEG_INF;
+  double W;
+  int anybad;
+  {
+    ResCtx X;
+    res_ctx(P, R, su, hs.mp, hs.mq, trow, drow, X);
+    const int c0 = c * CHUNK;
+    const int n = min(CHUNK, P.vocab - c0);
+    Seg<TT> sp;
+    Seg<TD> sq;
+    load_contig<TT>(tp + c0, n, tvec, NEG_INF, sp);
+    load_contig<TD>(dp + c0, n, dvec, qfill, sq);
+    bool bad = false;
+    double acc = 0.0;
+    if (logits) {
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) {
+        acc += resid_elem<true>(sp.at(i), sq.at(i), R, X);
+        if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound live fp64 temporaries
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) {
+        const float lq = sq.at(i);
+        acc += resid_elem<false>(sp.at(i), lq, R, X);
+        bad = bad || !(lq >= 0.f && lq < POS_INF);
+        if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    W = block_sum_d(acc, sm);
+    anybad = block_max_i(bad ? 1 : 0, sm);
+  }
+  if (!last) {
+    if (threadIdx.x == 0)
+      put_w(P.res + (int64_t)b * nc + c, anybad ? F_BAD : 0u, __float_as_uint((float)W));
+    return;
+  }
+  // last helper: collect the other chunks' residual masses, pick, draw
+  if (threadIdx.x == 0) {
+    hs.bad = anybad;
+    hs.timeout = 0;
+  }
+  __syncthreads();
+  int to = 0, bd = 0;
+  for (int cc = threadIdx.x; cc < nc - 1; cc += WG) {
+    const u64 v = take_w(P.res + (int64_t)b * nc + cc);
+    if (!(hi32(v) & TAG)) to = 1;
+    if (hi32(v) & F_BAD) bd = 1;
+    ds.E[cc] = (double)__uint_as_float(lo32(v));
+  }
+  if (threadIdx.x == 0) ds.E[nc - 1] = (double)(float)W;
+  if (to) atomicOr(&hs.timeout, 1);
+  if (bd) atomicOr(&hs.bad, 1);
+  __syncthreads();
+  const double u = (double)P.u[cu0 + k];
+  if (hs.timeout) {
+    write_fault(P, b, cu0, k, SV_ROW_INTERNAL);
+  } else if (hs.bad) {
+    write_fault(P, b, cu0, k, SV_ROW_NONFINITE);
+  } else if (!pick_chunk(nc, u, ds)) {
+    // residual mass is exactly zero: draw from p of the rejected row, using the
+    // row's chunk statistics (their payloads stay in the words after consumption)
+    const float tau = (P.thr_t && R.filt) ? thr_of(P.thr_t, trow) : NEG_INF;
+    const u64* cw = P.cst + (int64_t)trow * nc * 2;
+    const int t = draw_target_row<TT, AL>(
+        P, R, trow, su.Mp, -1, 0.f, tau, u,
+        [=](int cc) { return __uint_as_float(lo32(ld_agent(cw + 2 * cc))); },
+        [=](int cc) { return __uint_as_float(lo32(ld_agent(cw + 2 * cc + 1))); }, sm, ds);
+    if (threadIdx.x == 0) P.out[trow] = t;
+  } else {
+    const int ch = ds.chunk;
+    const double tl = ds.tl;
+    // the chosen chunk's maxima: from the decision payloads left in the words
+    const u64* dw = P.dec + ((int64_t)b * nc + ch) * 2;
+    const float mp = __uint_as_float(lo32(ld_agent(dw)));
+    const float mq = logits ? __uint_as_float(lo32(ld_agent(dw + 1))) : 0.f;
+    ResCtx X;
+    res_ctx(P, R, su, mp, mq, trow, drow, X);
+    const int c0 = ch * CHUNK;
+    const int n = min(CHUNK, P.vocab - c0);
+    int t;
+    if (logits) {
+      auto wf = [=](float lp, float lq, int) -> double { return resid_elem<true>(lp, lq, R, X); };
+      t = draw_chunk<TT, TD, true>(tp, dp, tvec, dvec, qfill, c0, n, tl, wf, sm, ds);
+    } else {
+      auto wf = [=](float lp, float lq, int) -> double { return resid_elem<false>(lp, lq, R, X); };
+      t = draw_chunk<TT, TD, true>(tp, dp, tvec, dvec, qfill, c0, n, tl, wf, sm, ds);
+    }
+    if (threadIdx.x == 0) P.out[trow] = t;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_verify: block index -> role
+//   The launch is a sequence of periods p = 0 .. batch: period p holds the
+//   producers of request p (p < batch; (max_k+1) * ns workgroups, row-major)
+//   followed by the helpers of request p-1 (p >= 1; H workgroups).
+// ---------------------------------------------------------------------------
+template <typename TT, typename TD, bool AL>
+__global__ __launch_bounds__(WG) void k_verify(const Params P) {
+  __shared__ Smem sm;
+  __shared__ FinShared fs;
+  __shared__ DrawShared ds;
+  __shared__ HelpShared hs;
+  extern __shared__ uint32_t stage[];
+  const int Pw = (P.max_k + 1) * P.ns;
+  const int H = P.H;
+  const long long id = blockIdx.x;
+  long long per, loc;
+  if (id < Pw) {
+    per = 0;
+    loc = id;
+  } else {
+    const long long rest = id - Pw;
+    const long long span = (long long)Pw + H;
+    const long long mid = (long long)(P.batch - 1) * span;
+    if (rest < mid) {
+      per = 1 + rest / span;
+      loc = rest % span;
+    } else {
+      per = P.batch;
+      loc = Pw + (rest - mid);
+    }
+  }
+  if (loc >= Pw) {   // helper of request per-1, chunk loc-Pw
+    helper<TT, TD, AL>(P, (int)per - 1, (int)(loc - Pw), sm, ds, hs);
+    return;
+  }
+  const int b = (int)per;
+  const int j = (int)(loc / P.ns);
+  const int s = (int)(loc % P.ns);
+  const int cu0 = P.cu[b];
+  const int cu1 = P.cu[b + 1];
+  const int k = cu1 - cu0 - 1;
+  if (!req_valid(P, b, cu0, cu1, k)) {
+    if (j == 0 && s == 0 && threadIdx.x == 0) {
+      P.accepted[b] = -1;
+      P.status[b] = SV_ROW_BAD_K;
+    }
+    return;
+  }
+  if (j > k) return;
+  const Req R = load_req(P, b);
+  if (!R.bad_param) produce<TT, TD, AL>(P, R, b, cu0, k, j, s, sm);
+  if (j == k && s == P.ns - 1) finalize<TT, TD, AL>(P, b, cu0, k, R, sm, fs, ds, stage);
+}
+
+// ---------------------------------------------------------------------------
+// k_thresh: top-k / top-p thresholds (one workgroup per filtered row)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t fkey(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;   // -0 and +0 are one value
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float keyf(uint32_t k) {
+  const uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+
+constexpr double FIX = 1099511627776.0;   // 2^40: fixed-point unit of masses
+
+struct ThrShared {
+  unsigned cnt[NWAVE][256];
+  unsigned long long mass[NWAVE][256];
+  int digit;
+  unsigned long long rem;
+  double remd;
+};
+
+template <typename T>
+__device__ float row_threshold(const T* __restrict__ rp, int V, int levels, const Req& R,
+                               Smem& sm, ThrShared& th) {
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  // pass A: max and number of finite values
+  float m = NEG_INF;
+  int nfin = 0;
+  for (int e = tid; e < V; e += WG) {
+    const float v = to_f(rp[e]);
+    m = fmax3nan(m, v);
+    nfin += (v > NEG_INF && v < POS_INF) ? 1 : 0;
+  }
+  const float M = block_max(m, sm);
+  // sum of counts via the fp64 reduction (exact for counts < 2^53)
+  const int NF = (int)block_sum_d((double)nfin, sm);
+  if (!(M > NEG_INF && M < POS_INF)) return NEG_INF;   // faults are reported by the row pass
+  const bool do_k = R.K > 0 && R.K < NF;
+  const bool do_p = R.P > 0.f && R.P < 1.f;
+  uint32_t tau_key = 0u;   // keep everything
+  if (do_k) {
+    uint32_t prefix = 0u, pmask = 0u;
+    unsigned remaining = (unsigned)R.K;
+    for (int lev = 0; lev < levels; ++lev) {
+      const int shift = 24 - 8 * lev;
+      for (int d = tid; d < 256 * NWAVE; d += WG) (&th.cnt[0][0])[d] = 0u;
+      __syncthreads();
+      for (int e = tid; e < V; e += WG) {
+        const float v = to_f(rp[e]);
+        if (!(v > NEG_INF)) continue;
+        const uint32_t key = fkey(v);
+        if ((key & pmask) != prefix) continue;
+        atomicAdd(&th.cnt[w][(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        unsigned above = 0u;
+        int dsel = 0;
+        for (int d = 255; d >= 0; --d) {
+          unsigned cd = 0u;
+          for (int q = 0; q < NWAVE; ++q) cd += th.cnt[q][d];
+          if (above + cd >= remaining) { dsel = d; break; }
+          above += cd;
+        }
+        th.digit = dsel;
+        th.rem = remaining - above;
+      }
+      __syncthreads();
+      remaining = (unsigned)th.rem;
+      prefix |= (uint32_t)th.digit << shift;
+      pmask |= 255u << shift;
+    }
+    tau_key = prefix;
+  }
+  if (do_p) {
+    const float tau_k = do_k ? keyf(tau_key) : NEG_INF;
+    const float off = chunk_off(M, R.c32);
+    uint32_t prefix = 0u, pmask = 0u;
+    double target = 0.0;
+    for (int lev = 0; lev < levels; ++lev) {
+      const int shift = 24 - 8 * lev;
+      for (int d = tid; d < 256 * NWAVE; d += WG) (&th.mass[0][0])[d] = 0ull;
+      __syncthreads();
+      for (int e = tid; e < V; e += WG) {
+        const float v = to_f(rp[e]);
+        if (!(v > NEG_INF) || v < tau_k) continue;
+        const uint32_t key = fkey(v);
+        if ((key & pmask) != prefix) continue;
+        const unsigned long long fx =
+            (unsigned long long)__double2ll_rn((double)eterm(v, R.c32, R.clo, off) * FIX);
+        atomicAdd(&th.mass[w][(key >> shift) & 255u], fx);
+      }
+      __syncthreads();
+      {
+        unsigned long long sacc = 0ull;
+        for (int q = 0; q < NWAVE; ++q) sacc += th.mass[q][tid];
+        __syncthreads();
+        th.mass[0][tid] = sacc;
+      }
+      __syncthreads();
+      if (tid == 0) {
+        unsigned long long Z = 0ull;
+        for (int d = 0; d < 256; ++d) Z += th.mass[0][d];
+        if (lev == 0) target = (double)R.P * (double)Z;
+        else target = th.remd;
+        double above = 0.0;
+        int dsel = -1, lastnz = -1;
+        for (int d = 255; d >= 0; --d) {
+          const unsigned long long td = th.mass[0][d];
+          if (td == 0ull) continue;
+          lastnz = d;
+          if (above + (double)td >= target) { dsel = d; break; }
+          above += (double)td;
+        }
+        if (dsel < 0) dsel = (lastnz >= 0) ? lastnz : 0;
+        th.digit = dsel;
+        th.remd = target - above;
+      }
+      __syncthreads();
+      prefix |= (uint32_t)th.digit << shift;
+      pmask |= 255u << shift;
+    }
+    tau_key = prefix > tau_key ? prefix : tau_key;
+  }
+  if (!do_k && !do_p) return NEG_INF;
+  return keyf(tau_key);
+}
+
+template <typename TT, typename TD>
+__global__ __launch_bounds__(WG) void k_thresh(const Params P) {
+  __shared__ Smem sm;
+  __shared__ ThrShared th;
+  int bid = blockIdx.x;
+  const int side = bid & 1;   // 0 target row, 1 draft row
+  bid >>= 1;
+  const int j = bid % (P.max_k + 1);
+  const int b = bid / (P.max_k + 1);
+  const int cu0 = P.cu[b];
+  const int cu1 = P.cu[b + 1];
+  const int k = cu1 - cu0 - 1;
+  if (!req_valid(P, b, cu0, cu1, k) || j > k) return;
+  const Req R = load_req(P, b);
+  if (R.greedy || R.bad_param || !R.filt) return;
+  if (side == 1 && (R.kind != SV_DRAFT_LOGITS || j >= k)) return;
+  float tau;
+  if (side == 0) {
+    const TT* rp = (const TT*)P.target + (int64_t)(cu0 + j) * P.ld_t;
+    tau = row_threshold<TT>(rp, P.vocab, sizeof(TT) == 2 ? 2 : 4, R, sm, th);
+    if (threadIdx.x == 0) P.thr_t[cu0 + j] = (u64)__float_as_uint(tau);
+  } else {
+    const TD* rp = (const TD*)P.draft + (int64_t)(cu0 - b + j) * P.ld_d;
+    tau = row_threshold<TD>(rp, P.vocab, sizeof(TD) == 2 ? 2 : 4, R, sm, th);
+    if (threadIdx.x == 0) P.thr_d[cu0 - b + j] = (u64)__float_as_uint(tau);
+  }
+}
+
+__global__ void k_fill_zero(uint4* p, size_t n16, unsigned char* tail, size_t ntail) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t q = i; q < n16; q += stride) p[q] = make_uint4(0u, 0u, 0u, 0u);
+  if (i < ntail) tail[i] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+struct Layout {
+  size_t cst, dst, rx, setup, dec, res, thr_t, thr_d, total;
+};
+
+static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static bool layout(int batch, int total_rows, int vocab, int max_k, Layout& L, int& nc) {
+  if (batch < 1 || total_rows < batch || vocab < 1 || max_k < 0 || max_k > MAX_K) return false;
+  nc = (vocab + CHUNK - 1) / CHUNK;
+  if (nc > MAX_NC) return false;
+  if ((size_t)8 * (2 * max_k + 1) * nc > (size_t)STAGE_MAX) return false;
+  const size_t B = (size_t)batch, R = (size_t)total_rows, D = (size_t)(total_rows - batch);
+  const size_t D1 = D ? D : 1;
+  size_t o = 0;
+  L.cst = o; o = align_up(o + R * nc * 2 * sizeof(u64));
+  L.dst = o; o = align_up(o + D1 * nc * 2 * sizeof(u64));
+  L.rx = o; o = align_up(o + R * 3 * sizeof(u64));
+  L.setup = o; o = align_up(o + B * sizeof(SetupWords));
+  L.dec = o; o = align_up(o + B * nc * 2 * sizeof(u64));
+  L.res = o; o = align_up(o + B * nc * sizeof(u64));
+  L.thr_t = o; o = align_up(o + R * sizeof(u64));
+  L.thr_d = o; o = align_up(o + D1 * sizeof(u64));
+  L.total = o;
+  return true;
+}
+
+template <typename TT>
+static long long verify_grid(const Params& P) {
+  return (long long)P.batch * (P.max_k + 1) * P.ns + (long long)P.batch * P.H;
+}
+
+template <typename TT, typename TD>
+static int launch_all(Params P, bool sampled, bool filters, bool aligned, hipStream_t st) {
+  P.S = Strip<TT>::S;
+  P.ns = (P.nc + P.S - 1) / P.S;
+  P.H = sampled ? P.nc : 0;
+  const long long g = verify_grid<TT>(P);
+  if (g >= (1LL << 31)) return SV_ERR_SHAPE;
+  const size_t lds = (size_t)8 * (2 * P.max_k + 1) * P.nc;
+  if (filters) {
+    const long long g0 = (long long)P.batch * (P.max_k + 1) * 2;
+    hipLaunchKernelGGL((k_thresh<TT, TD>), dim3((unsigned)g0), dim3(WG), 0, st, P);
+  }
+  if (aligned)
+    hipLaunchKernelGGL((k_verify<TT, TD, true>), dim3((unsigned)g), dim3(WG), lds, st, P);
+  else
+    hipLaunchKernelGGL((k_verify<TT, TD, false>), dim3((unsigned)g), dim3(WG), lds, st, P);
+  return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+}
+
+// Rows take 128-bit loads when the buffer's base address and row pitch are
+// multiples of 16 bytes.
+static bool rows_aligned(const void* base, int64_t ld, int elem) {
+  return base == nullptr || (((uintptr_t)base & 15) == 0 && ((ld * elem) & 15) == 0);
+}
+
+static int dispatch(const Params& P, int tdt, int ddt, bool sampled, bool filters,
+                    hipStream_t st) {
+  const bool al = rows_aligned(P.target, P.ld_t, tdt == SV_F32 ? 4 : 2) &&
+                  rows_aligned(P.draft, P.ld_d, ddt == SV_F32 ? 4 : 2);
+  if (tdt == SV_F32 && ddt == SV_F32)
+    return launch_all<float, float>(P, sampled, filters, al, st);
+  if (tdt == SV_F32 && ddt == SV_BF16)
+    return launch_all<float, uint16_t>(P, sampled, filters, al, st);
+  if (tdt == SV_BF16 && ddt == SV_F32)
+    return launch_all<uint16_t, float>(P, sampled, filters, al, st);
+  return launch_all<uint16_t, uint16_t>(P, sampled, filters, al, st);
+}
+
+static bool grid_ok(int batch, int max_k, int nc) {
+  // strips of one chunk are the worst case
+  const long long g = (long long)batch * (max_k + 1) * nc + (long long)batch * nc;
+  return g < (1LL << 31);
+}
+
+static void carve(Params& P, void* ws, const Layout& L) {
+  char* w = (char*)ws;
+  P.cst = (u64*)(w + L.cst);
+  P.dst = (u64*)(w + L.dst);
+  P.rx = (u64*)(w + L.rx);
+  P.setup = (SetupWords*)(w + L.setup);
+  P.dec = (u64*)(w + L.dec);
+  P.res = (u64*)(w + L.res);
+  P.thr_t = (u64*)(w + L.thr_t);
+  P.thr_d = (u64*)(w + L.thr_d);
+}
+
+}  // namespace sv
+
+using namespace sv;
+
+extern "C" {
+
+int spec_verify_abi_version(void) { return SPECVERIFY_ABI_VERSION; }
+
+const char* spec_verify_status_string(int code) {
+  switch (code) {
+    case SV_OK: return "ok";
+    case SV_ERR_NULL: return "a required pointer is NULL";
+    case SV_ERR_SHAPE: return "invalid sizes (batch, total_rows, max_k, vocab or ld)";
+    case SV_ERR_DTYPE: return "unknown dtype code";
+    case SV_ERR_WORKSPACE: return "workspace smaller than spec_verify_workspace_bytes()";
+    case SV_ERR_LAUNCH: return "kernel launch failed";
+    case 100 + SV_ROW_OK: return "row ok";
+    case 100 + SV_ROW_NONFINITE: return "row: NaN/inf logit or invalid probability";
+    case 100 + SV_ROW_EMPTY: return "row: no finite logit";
+    case 100 + SV_ROW_BAD_K: return "row: offsets out of range or k > max_k";
+    case 100 + SV_ROW_BAD_TOKEN: return "row: draft id outside [0, vocab)";
+    case 100 + SV_ROW_BAD_PARAM: return "row: bad draft kind or temperature";
+    case 100 + SV_ROW_INTERNAL: return "row: internal wait ran out (re-initialise the workspace)";
+    default: return "unknown code";
+  }
+}
+
+size_t spec_verify_workspace_bytes(int batch, int total_rows, int vocab, int max_k) {
+  Layout L;
+  int nc;
+  if (!layout(batch, total_rows, vocab, max_k, L, nc)) return 0;
+  return L.total;
+}
+
+int spec_verify_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace) return SV_ERR_NULL;
+  if (workspace_bytes == 0) return SV_OK;
+  const size_t n16 = workspace_bytes / 16;
+  const size_t ntail = workspace_bytes - n16 * 16;
+  unsigned blocks = (unsigned)((n16 + 255) / 256);
+  if (blocks > 4096) blocks = 4096;
+  if (blocks == 0) blocks = 1;
+  hipLaunchKernelGGL(k_fill_zero, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                     (uint4*)workspace, n16, (unsigned char*)workspace + n16 * 16, ntail);
+  return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+}
+
+int spec_verify_greedy(const void* target_logits, int target_dtype, int64_t ld_target,
+                       const int32_t* cu_seqlens, const int32_t* draft_tokens, int batch,
+                       int total_rows, int max_k, int vocab, int32_t* accepted,
+                       int32_t* out_tokens, int32_t* status, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (!target_logits || !cu_seqlens || !accepted || !out_tokens || !status || !workspace)
+    return SV_ERR_NULL;
+  if (!draft_tokens && total_rows > batch) return SV_ERR_NULL;
+  if (target_dtype != SV_F32 && target_dtype != SV_BF16) return SV_ERR_DTYPE;
+  Layout L;
+  int nc;
+  if (!layout(batch, total_rows, vocab, max_k, L, nc) || ld_target < vocab ||
+      !grid_ok(batch, max_k, nc))
+    return SV_ERR_SHAPE;
+  if (workspace_bytes < L.total) return SV_ERR_WORKSPACE;
+  Params P = {};
+  P.target = target_logits;
+  P.cu = cu_seqlens;
+  P.drafts = draft_tokens;
+  P.accepted = accepted;
+  P.out = out_tokens;
+  P.status = status;
+  P.ld_t = ld_target;
+  P.ld_d = 0;
+  P.batch = batch;
+  P.total_rows = total_rows;
+  P.max_k = max_k;
+  P.vocab = vocab;
+  P.nc = nc;
+  P.greedy_entry = 1;
+  carve(P, workspace, L);
+  P.thr_t = nullptr;
+  P.thr_d = nullptr;
+  return dispatch(P, target_dtype, SV_BF16, false, false, (hipStream_t)stream);
+}
+
+int spec_verify_sampled(const void* target_logits, int target_dtype, int64_t ld_target,
+                        const void* draft, int draft_dtype, int64_t ld_draft,
+                        const int32_t* draft_kind, const int32_t* cu_seqlens,
+                        const int32_t* draft_tokens, const float* uniforms,
+                        const float* temperature, const int32_t* top_k, const float* top_p,
+                        int batch, int total_rows, int max_k, int vocab, int32_t* accepted,
+                        int32_t* out_tokens, float* p_at_draft, float* q_at_draft,
+                        int32_t* status, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (!target_logits || !draft_kind || !cu_seqlens || !uniforms || !temperature || !accepted ||
+      !out_tokens || !status || !workspace)
+    return SV_ERR_NULL;
+  if (!draft_tokens && total_rows > batch) return SV_ERR_NULL;
+  if (target_dtype != SV_F32 && target_dtype != SV_BF16) return SV_ERR_DTYPE;
+  if (draft && draft_dtype != SV_F32 && draft_dtype != SV_BF16) return SV_ERR_DTYPE;
+  Layout L;
+  int nc;
+  if (!layout(batch, total_rows, vocab, max_k, L, nc) || ld_target < vocab ||
+      (draft && ld_draft < vocab) || !grid_ok(batch, max_k, nc))
+    return SV_ERR_SHAPE;
+  if (workspace_bytes < L.total) return SV_ERR_WORKSPACE;
+  Params P = {};
+  P.target = target_logits;
+  P.draft = draft;
+  P.kind = draft_kind;
+  P.cu = cu_seqlens;
+  P.drafts = draft_tokens;
+  P.u = uniforms;
+  P.temp = temperature;
+  P.top_k = top_k;
+  P.top_p = top_p;
+  P.accepted = accepted;
+  P.out = out_tokens;
+  P.p_at = p_at_draft;
+  P.q_at = q_at_draft;
+  P.status = status;
+  P.ld_t = ld_target;
+  P.ld_d = draft ? ld_draft : 0;
+  P.batch = batch;
+  P.total_rows = total_rows;
+  P.max_k = max_k;
+  P.vocab = vocab;
+  P.nc = nc;
+  P.greedy_entry = 0;
+  carve(P, workspace, L);
+  const bool filters = top_k != nullptr || top_p != nullptr;
+  if (!filters) {
+    P.thr_t = nullptr;
+    P.thr_d = nullptr;
+  }
+  const int ddt = draft ? draft_dtype : target_dtype;
+  return dispatch(P, target_dtype, ddt, true, filters, (hipStream_t)stream);
+}
+
+}  // extern "C"
