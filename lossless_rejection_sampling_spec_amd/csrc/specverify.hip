@@ -33,12 +33,15 @@
 // bounded (a request whose wait runs out reports SV_ROW_INTERNAL).  A
 // workspace is therefore left with no tag set when a call ends.
 //
-// Numerics (temperature T, c = log2(e)/T split as c32 + clo with clo > 0):
-//   element term    e = exp2(fma(l, clo, fma(l, c32, -off_c))), off_c = m_c*c32
-//                   in fp32, m_c the chunk max; summed per thread in fp32 and
-//                   across threads in fp64, published as fp32.
-//   chunk merge     S = sum_c s_c * exp2(off_c - M*c) in fp64, in chunk order.
-//   gathered p(x)   exp2((l_x - M)*c) / S in fp64; acceptance u*q(x) < p(x)
+// Numerics (temperature T, c = log2(e)/T rounded to fp32; every fp64 step
+// uses that same c, so all terms share one temperature):
+//   element term    exp2((l - r) * c) in fp32 against a reference r >= l (a
+//                   thread's own max in the producers, the chunk max elsewhere).
+//   chunk sum       s_c = sum over threads of (fp32 sum of the thread's terms)
+//                   * exp2((m_t - m_c) * c), rescaled and added in fp64 and
+//                   published as fp32 with the chunk max m_c.
+//   chunk merge     S = sum_c s_c * exp2((m_c - M) * c) in fp64, in chunk order.
+//   gathered p(x)   exp2((l_x - M) * c) / S in fp64; acceptance u*q(x) < p(x)
 //                   in fp64.
 //   final draw      chunk masses in fp64, sequential prefix over chunks, then a
 //                   fp64 block scan over the chosen chunk in token order.
@@ -386,8 +389,8 @@ struct Req {
   int K;
   float P;
   bool filt;
-  double ce;  // c32 + clo, the multiplier the element terms use
-  float c32, clo;
+  float c;    // log2(e) / T rounded to fp32
+  double ce;  // the same value in fp64
 };
 
 __device__ __forceinline__ Req load_req(const Params& P, int b) {
@@ -403,15 +406,11 @@ __device__ __forceinline__ Req load_req(const Params& P, int b) {
   if (R.K >= P.vocab) R.K = 0;
   R.filt = R.K > 0 || (R.P > 0.f && R.P < 1.f);
   if (!R.greedy && !R.bad_param) {
-    const double ce = LOG2E / (double)R.T;
-    const float c32 = __double2float_rd(ce);
-    float clo = (float)(ce - (double)c32);
-    clo = fmaxf(clo, FLT_MIN);   // strictly positive: -inf * clo stays -inf
-    R.c32 = c32;
-    R.clo = clo;
-    R.ce = (double)c32 + (double)clo;
+    R.c = (float)(LOG2E / (double)R.T);   // finite and > 0 for FLT_MIN <= T < inf
+    R.ce = (double)R.c;
   } else {
-    R.c32 = 0.f; R.clo = 0.f; R.ce = 0.0;
+    R.c = 0.f;
+    R.ce = 0.0;
   }
   return R;
 }
@@ -425,10 +424,14 @@ __device__ __forceinline__ float thr_of(const u64* t, int i) {
   return __uint_as_float((uint32_t)t[i]);
 }
 
-__device__ __forceinline__ float chunk_off(float m, float c32) { return m * c32; }
+// exp2((v - r) * c) for v <= r, r finite (v = -inf gives 0)
+__device__ __forceinline__ float term(float v, float r, float c) {
+  return __builtin_amdgcn_exp2f((v - r) * c);
+}
 
-__device__ __forceinline__ float eterm(float v, float c32, float clo, float off) {
-  return __builtin_amdgcn_exp2f(__builtin_fmaf(v, clo, __builtin_fmaf(v, c32, -off)));
+// exp2((m - M) * c) in fp64 (the scale of a chunk with max m in a row with max M)
+__device__ __forceinline__ double scale_d(float m, float M, double ce) {
+  return exp2(((double)m - (double)M) * ce);
 }
 
 // ---------------------------------------------------------------------------
@@ -441,56 +444,87 @@ struct CStat {
   int arg;     // lowest index of the max within the chunk (greedy rows)
 };
 
-// Statistics of one chunk held in the strided layout.  VF(i) gives the value
-// of slot i (masked to -inf below a top-k/top-p threshold when there is one).
-// xl: chunk-local index of the draft id, or -1.
-template <typename T, typename VF>
-__device__ __forceinline__ CStat chunk_stats_v(VF val, bool greedy, float c32, float clo, int xl,
-                                               Smem& sm) {
-  float m = NEG_INF;
-#pragma unroll
-  for (int i = 0; i < EPT; ++i) m = fmax3nan(m, val(i));
-  const float M = block_max(m, sm);
-  CStat st;
-  st.m = M;
-  st.s = 0.f;
-  st.sx = 0.f;
-  st.arg = INT32_MAX;
-  if (greedy) {
-    int cand = INT32_MAX;
-    if (m == M) {   // only the threads that hold the chunk max search for its first slot
-      int slot = EPT;
-#pragma unroll
-      for (int i = EPT - 1; i >= 0; --i) slot = (val(i) == M) ? i : slot;
-      cand = strided_index<T>(slot);
-    }
-    st.arg = block_min_i(cand, sm);
-  } else if (M > NEG_INF && M < POS_INF) {
-    const float off = chunk_off(M, c32);
-    float acc = 0.f;
-    if (xl < 0) {
-#pragma unroll
-      for (int i = 0; i < EPT; ++i) acc += eterm(val(i), c32, clo, off);
-      st.s = (float)block_sum_d((double)acc, sm);
-    } else {
-      // the thread that holds element xl also sums its terms without it
-      constexpr int VEC = VT<T>::VEC;
-      const int owner = (xl / VEC) % WG;
-      const int xslot = ((xl / VEC) / WG) * VEC + xl % VEC;
-      const int ix = ((int)threadIdx.x == owner) ? xslot : -1;
-      float accx = 0.f;
-#pragma unroll
-      for (int i = 0; i < EPT; ++i) {
-        const float e = eterm(val(i), c32, clo, off);
-        acc += e;
-        accx += (i == ix) ? 0.f : e;
-      }
-      st.s = (float)block_sum_d((double)acc, sm);
-      st.sx = (float)block_sum_d((double)accx, sm);
-    }
-  }
-  return st;
+// ---- wave reductions over DPP: rows of 16 lanes by butterflies, then the four
+// rows read back as scalars (the result is uniform across the wave)
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xf, 0xf, false);
 }
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(x)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double x) {
+  const long long v = __double_as_longlong(x);
+  const int lo = dpp_i<CTRL>((int)(uint32_t)v);
+  const int hi = dpp_i<CTRL>((int)(uint32_t)(v >> 32));
+  return __longlong_as_double((long long)(((u64)(uint32_t)hi << 32) | (u64)(uint32_t)lo));
+}
+constexpr int DPP_XOR1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int DPP_HMIRROR = 0x141;  // lane i <-> 7 - i within each 8
+constexpr int DPP_MIRROR = 0x140;   // lane i <-> 15 - i within each 16
+
+__device__ __forceinline__ float rl_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+__device__ __forceinline__ double rl_d(double x, int l) {
+  const long long v = __double_as_longlong(x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return __longlong_as_double((long long)(((u64)hi << 32) | lo));
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmax3nan(x, dpp_f<DPP_XOR1>(x));
+  x = fmax3nan(x, dpp_f<DPP_XOR2>(x));
+  x = fmax3nan(x, dpp_f<DPP_HMIRROR>(x));
+  x = fmax3nan(x, dpp_f<DPP_MIRROR>(x));
+  return fmax3nan(fmax3nan(rl_f(x, 0), rl_f(x, 16)), fmax3nan(rl_f(x, 32), rl_f(x, 48)));
+}
+
+// Sum in a fixed tree order (lane pairs, quads, halves, rows, then rows 0..3).
+__device__ __forceinline__ double wave_sum(double x) {
+  x += dpp_d<DPP_XOR1>(x);
+  x += dpp_d<DPP_XOR2>(x);
+  x += dpp_d<DPP_HMIRROR>(x);
+  x += dpp_d<DPP_MIRROR>(x);
+  return (rl_d(x, 0) + rl_d(x, 16)) + (rl_d(x, 32) + rl_d(x, 48));
+}
+
+// (max, lowest index of the max); NaN propagates with index INT32_MAX
+__device__ __forceinline__ void arg_step(float& m, int& i, float mo, int io) {
+  const float mm = fmax3nan(m, mo);
+  i = min(m == mm ? i : INT32_MAX, mo == mm ? io : INT32_MAX);
+  m = mm;
+}
+template <int CTRL>
+__device__ __forceinline__ void arg_dpp(float& m, int& i) {
+  arg_step(m, i, dpp_f<CTRL>(m), dpp_i<CTRL>(i));
+}
+__device__ __forceinline__ void wave_argmax(float& m, int& i) {
+  arg_dpp<DPP_XOR1>(m, i);
+  arg_dpp<DPP_XOR2>(m, i);
+  arg_dpp<DPP_HMIRROR>(m, i);
+  arg_dpp<DPP_MIRROR>(m, i);
+  float m0 = rl_f(m, 0);
+  int i0 = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+  for (int r = 16; r < 64; r += 16) arg_step(m0, i0, rl_f(m, r), __builtin_amdgcn_readlane(i, r));
+  m = m0;
+  i = i0;
+}
+
+// LDS of the producer reductions: two slot sets used alternately by
+// consecutive chunks, so each reduction needs a single barrier.
+struct ProdShared {
+  float m[2][NWAVE];
+  int i[2][NWAVE];
+  double s[2][NWAVE];
+  double sx[2][NWAVE];
+  uint32_t pub[16][3];   // per task: max, sum or index, sum without x
+};
 
 // Mask, in place, every element below tau (a top-k / top-p threshold) to -inf.
 // NaN compares false and is kept, so the fault is still seen.
@@ -517,23 +551,99 @@ template <> __device__ __forceinline__ void apply_tau<uint16_t>(Seg<uint16_t>& s
   }
 }
 
-template <typename T>
-__device__ __forceinline__ CStat chunk_stats(Seg<T>& sg, bool greedy, float tau, float c32,
-                                             float clo, int xl, Smem& sm) {
-  if (tau > NEG_INF) apply_tau<T>(sg, tau);
-  auto val = [&](int i) { return sg.at(i); };
-  return chunk_stats_v<T>(val, greedy, c32, clo, xl, sm);
-}
 
-__device__ __forceinline__ void publish_stat(u64* w, const CStat& st, bool greedy) {
-  put_w(w, 0u, __float_as_uint(st.m));
-  put_w(w + 1, 0u, greedy ? (uint32_t)st.arg : __float_as_uint(st.s));
+// Statistics of one chunk held in the strided layout (slot i of the thread is
+// chunk element strided_index(i)).  xl: chunk-local index of the draft id, or
+// -1.  par: the slot set of this chunk.  All threads return the same values.
+template <typename T>
+__device__ __forceinline__ CStat chunk_stats(Seg<T>& sg, bool greedy, float tau, float c, int xl,
+                                             int par, ProdShared& ps) {
+  if (tau > NEG_INF) apply_tau<T>(sg, tau);
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  float m = NEG_INF;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) m = fmax3nan(m, sg.at(i));
+  CStat st;
+  st.s = 0.f;
+  st.sx = 0.f;
+  st.arg = INT32_MAX;
+  if (greedy) {
+    int slot = EPT;
+#pragma unroll
+    for (int i = EPT - 1; i >= 0; --i) slot = (sg.at(i) == m) ? i : slot;
+    float wm = m;
+    int wi = slot < EPT ? strided_index<T>(slot) : INT32_MAX;
+    wave_argmax(wm, wi);
+    if (lane == 0) {
+      ps.m[par][w] = wm;
+      ps.i[par][w] = wi;
+    }
+    __syncthreads();
+    float bm = ps.m[par][0];
+    int bi = ps.i[par][0];
+#pragma unroll
+    for (int q = 1; q < NWAVE; ++q) arg_step(bm, bi, ps.m[par][q], ps.i[par][q]);
+    st.m = bm;
+    st.arg = bi;
+    return st;
+  }
+  const float wm = wave_max(m);
+  if (lane == 0) ps.m[par][w] = wm;
+  // the terms against the thread's own max need no block result: they run
+  // while the other waves reach the barrier
+  float acc = 0.f, accx = 0.f;
+  const bool own = m > NEG_INF && m < POS_INF;
+  if (xl < 0) {
+    if (own) {
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) acc += term(sg.at(i), m, c);
+    }
+  } else {
+    constexpr int VEC = VT<T>::VEC;
+    const int owner = (xl / VEC) % WG;
+    const int xslot = ((xl / VEC) / WG) * VEC + xl % VEC;
+    const int ix = ((int)threadIdx.x == owner) ? xslot : -1;
+    if (own) {
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) {
+        const float e = term(sg.at(i), m, c);
+        acc += e;
+        accx += (i == ix) ? 0.f : e;
+      }
+    }
+  }
+  __syncthreads();
+  float M = ps.m[par][0];
+#pragma unroll
+  for (int q = 1; q < NWAVE; ++q) M = fmax3nan(M, ps.m[par][q]);
+  st.m = M;
+  if (!(M > NEG_INF && M < POS_INF)) return st;   // empty chunk or a data fault
+  const double f = own ? (double)term(m, M, c) : 0.0;
+  const double ws = wave_sum((double)acc * f);
+  double wsx = 0.0;
+  if (xl >= 0) wsx = wave_sum((double)accx * f);
+  if (lane == 0) {
+    ps.s[par][w] = ws;
+    ps.sx[par][w] = wsx;
+  }
+  __syncthreads();
+  double S = 0.0, SX = 0.0;
+#pragma unroll
+  for (int q = 0; q < NWAVE; ++q) {
+    S += ps.s[par][q];
+    SX += ps.sx[par][q];
+  }
+  st.s = (float)S;
+  st.sx = (float)SX;
+  return st;
 }
 
 // chunks per producer strip (64 KiB of bf16 or fp32 target data)
 template <typename TT> struct Strip;
 template <> struct Strip<uint16_t> { static constexpr int S = 4; };
 template <> struct Strip<float> { static constexpr int S = 2; };
+static_assert(Strip<uint16_t>::S <= 8 && Strip<float>::S <= 8, "strip too long");
 
 // Words of one chunk of either element type (sized for the wider one).
 template <typename TT, typename TD>
@@ -551,24 +661,45 @@ __device__ __forceinline__ void buf_issue(const T* __restrict__ cp, int n, bool 
   for (int i = 0; i < Seg<T>::NV; ++i) b.q[i] = sg.q[i];
 }
 
-template <typename T, typename TT, typename TD>
-__device__ __forceinline__ CStat buf_stats(const Buf<TT, TD>& b, int n, bool al, bool greedy,
-                                           float tau, float c32, float clo, int xl, Smem& sm) {
+template <typename TT, typename TD, bool AL>
+__device__ __forceinline__ void issue_task(const TT* trow, const TD* drow, bool is_d, int c,
+                                           int vocab, Buf<TT, TD>& bf) {
+  const int n = min(CHUNK, vocab - c * CHUNK);
+  if (is_d) buf_issue<TD>(drow + c * CHUNK, n, AL, bf);
+  else buf_issue<TT>(trow + c * CHUNK, n, AL, bf);
+}
+
+// One producer task: the statistics of chunk c of the target row (is_d false)
+// or of the draft-logit row, kept in LDS (slot t) until the strip ends.
+template <typename T, typename TT, typename TD, bool AL>
+__device__ __forceinline__ void produce_task(const Params& P, const Req& R, const Buf<TT, TD>& bf,
+                                             bool is_d, int c, int x, float tau, int t,
+                                             ProdShared& ps) {
+  const int c0 = c * CHUNK;
+  const int n = min(CHUNK, P.vocab - c0);
+  const bool xin = !is_d && x >= c0 && x < c0 + n;
   Seg<T> sg;
 #pragma unroll
-  for (int i = 0; i < Seg<T>::NV; ++i) sg.q[i] = b.q[i];
-  finish_words<T>(n, al, NEG_INF, [](int i) { return strided_off<T>(i); }, sg);
-  return chunk_stats<T>(sg, greedy, tau, c32, clo, xl, sm);
+  for (int i = 0; i < Seg<T>::NV; ++i) sg.q[i] = bf.q[i];
+  finish_words<T>(n, AL, NEG_INF, [](int i) { return strided_off<T>(i); }, sg);
+  const bool greedy = R.greedy && !is_d;
+  const CStat st = chunk_stats<T>(sg, greedy, tau, R.c, xin ? x - c0 : -1, t & 1, ps);
+  if (threadIdx.x == 0) {
+    ps.pub[t][0] = __float_as_uint(st.m);
+    ps.pub[t][1] = greedy ? (uint32_t)st.arg : __float_as_uint(st.s);
+    ps.pub[t][2] = __float_as_uint(st.sx);
+  }
 }
 
 // Producer of request b, row j, strip s: statistics of S chunks of the target
-// row (and of the draft row for draft-logit requests).  The chunks are a
-// two-deep pipeline of tasks (target chunk, then draft chunk when there is one):
-// task i+1's loads are issued before task i is reduced.
+// row (and of the draft row for draft-logit requests).  The tasks (a target
+// chunk, then the draft chunk when there is one) run through two buffers: the
+// loads of task t+1 are issued before task t is reduced.  Every step issues
+// a load (the last task's is repeated) so the wait before each reduction only
+// covers the buffer it reads; the hand-off words are written after the strip.
 template <typename TT, typename TD, bool AL>
 __device__ __forceinline__ void produce(const Params& P, const Req& R, int b, int cu0, int k,
-                                        int j, int s, Smem& sm) {
-  constexpr int S = Strip<TT>::S;
+                                        int j, int s, ProdShared& ps, Buf<TT, TD>& A) {
   const int nc = P.nc;
   const int row = cu0 + j;
   const int d0 = cu0 - b;
@@ -578,51 +709,61 @@ __device__ __forceinline__ void produce(const Params& P, const Req& R, int b, in
   const TD* drow = (const TD*)P.draft + (int64_t)(d0 + j) * P.ld_d;
   const float taud = (has_d && P.thr_d && R.filt) ? thr_of(P.thr_d, d0 + j) : NEG_INF;
   const int x = (!R.greedy && j < k) ? P.drafts[d0 + j] : -1;
-  const int c_begin = s * S;
-  const int c_end = min(c_begin + S, nc);
-  const int per = has_d ? 2 : 1;
-  const int nt = (c_end - c_begin) * per;
+  const int c_begin = s * P.S;
+  const int c_end = min(c_begin + P.S, nc);
+  const int sh = has_d ? 1 : 0;   // task t: chunk c_begin + (t >> sh), draft iff t & sh
+  const int nt = (c_end - c_begin) << sh;
+  // the single values at the draft id, gathered by thread 0 and published
+  // after the strip (issued first, they wait behind nothing)
+  const bool xs = threadIdx.x == 0 && x >= c_begin * CHUNK && x < min(c_end * CHUNK, P.vocab);
+  TT lx_raw = TT(0);
+  TD ldx_raw = TD(0);
+  if (xs) {
+    lx_raw = trow[x];
+    if (R.kind != SV_DRAFT_ONEHOT) ldx_raw = drow[x];
+  }
 
-  Buf<TT, TD> cur, nxt;
-  buf_issue<TT>(trow + c_begin * CHUNK, min(CHUNK, P.vocab - c_begin * CHUNK), AL, cur);
-  for (int t = 0; t < nt; ++t) {
-    const int c = c_begin + t / per;
-    const bool is_d = has_d && (t & 1);
+  Buf<TT, TD> B;   // A holds the first task's loads (issued by the caller)
+  int t = 0;
+  for (; t + 1 < nt; t += 2) {
+    const int t1 = t + 1;
+    issue_task<TT, TD, AL>(trow, drow, (t1 & sh) != 0, c_begin + (t1 >> sh), P.vocab, B);
+    if ((t & sh) == 0)
+      produce_task<TT, TT, TD, AL>(P, R, A, false, c_begin + (t >> sh), x, tau, t, ps);
+    else
+      produce_task<TD, TT, TD, AL>(P, R, A, true, c_begin + (t >> sh), x, taud, t, ps);
+    const int t2 = min(t + 2, nt - 1);
+    issue_task<TT, TD, AL>(trow, drow, (t2 & sh) != 0, c_begin + (t2 >> sh), P.vocab, A);
+    if ((t1 & sh) == 0)
+      produce_task<TT, TT, TD, AL>(P, R, B, false, c_begin + (t1 >> sh), x, tau, t1, ps);
+    else
+      produce_task<TD, TT, TD, AL>(P, R, B, true, c_begin + (t1 >> sh), x, taud, t1, ps);
+  }
+  if (t < nt) {   // odd count: the last task is a target chunk, already in A
+    produce_task<TT, TT, TD, AL>(P, R, A, false, c_begin + (t >> sh), x, tau, t, ps);
+  }
+  __syncthreads();
+  const int tp = threadIdx.x;
+  if (tp < nt) {
+    const bool is_d = (tp & sh) != 0;
+    const int c = c_begin + (tp >> sh);
+    u64* w = is_d ? P.dst + ((int64_t)(d0 + j) * nc + c) * 2 : P.cst + ((int64_t)row * nc + c) * 2;
+    put_w(w, 0u, ps.pub[tp][0]);
+    put_w(w + 1, 0u, ps.pub[tp][1]);
     const int c0 = c * CHUNK;
-    const int n = min(CHUNK, P.vocab - c0);
-    if (t + 1 < nt) {   // next task's loads go out before this one is reduced
-      const int cn = c_begin + (t + 1) / per;
-      const int nn = min(CHUNK, P.vocab - cn * CHUNK);
-      if (has_d && ((t + 1) & 1)) buf_issue<TD>(drow + cn * CHUNK, nn, AL, nxt);
-      else buf_issue<TT>(trow + cn * CHUNK, nn, AL, nxt);
+    if (!is_d && x >= c0 && x < c0 + min(CHUNK, P.vocab - c0))
+      put_w(P.rx + (int64_t)row * 3 + 1, 0u, ps.pub[tp][2]);
+  }
+  if (xs) {
+    float lx = to_f(lx_raw), ldx = to_f(ldx_raw);
+    if (lx < tau) lx = NEG_INF;
+    put_w(P.rx + (int64_t)row * 3 + 0, 0u, __float_as_uint(lx));
+    if (R.kind == SV_DRAFT_PROBS) {
+      put_w(P.rx + (int64_t)row * 3 + 2, 0u, __float_as_uint(ldx));
+    } else if (R.kind == SV_DRAFT_LOGITS) {
+      if (ldx < taud) ldx = NEG_INF;
+      put_w(P.rx + (int64_t)row * 3 + 2, 0u, __float_as_uint(ldx));
     }
-    const bool xin = x >= c0 && x < c0 + n;
-    if (!is_d) {
-      const CStat st = buf_stats<TT>(cur, n, AL, R.greedy, tau, R.c32, R.clo,
-                                     xin ? x - c0 : -1, sm);
-      if (threadIdx.x == 0) {
-        publish_stat(P.cst + ((int64_t)row * nc + c) * 2, st, R.greedy);
-        if (xin) {
-          float lx = to_f(trow[x]);
-          if (lx < tau) lx = NEG_INF;
-          put_w(P.rx + (int64_t)row * 3 + 0, 0u, __float_as_uint(lx));
-          put_w(P.rx + (int64_t)row * 3 + 1, 0u, __float_as_uint(st.sx));
-        }
-        if (R.kind == SV_DRAFT_PROBS && j < k && xin)
-          put_w(P.rx + (int64_t)row * 3 + 2, 0u, __float_as_uint(to_f(drow[x])));
-      }
-    } else {
-      const CStat sd = buf_stats<TD>(cur, n, AL, false, taud, R.c32, R.clo, -1, sm);
-      if (threadIdx.x == 0) {
-        publish_stat(P.dst + ((int64_t)(d0 + j) * nc + c) * 2, sd, false);
-        if (xin) {
-          float dlx = to_f(drow[x]);
-          if (dlx < taud) dlx = NEG_INF;
-          put_w(P.rx + (int64_t)row * 3 + 2, 0u, __float_as_uint(dlx));
-        }
-      }
-    }
-    cur = nxt;
   }
 }
 
@@ -736,25 +877,19 @@ __device__ __forceinline__ bool pick_chunk(int nc, double u, DrawShared& ds) {
 
 
 // Draw from p of one target row (bonus draw, one-hot rejection with
-// `exclude` = the rejected draft id, zero-residual fallback).  cm(c) and
-// cs(c) give chunk c's max and sum of terms (cs_x: the sum of x's chunk
-// without x); M is the merged row max.  Returns the token (all threads).
-template <typename TT, bool AL, typename FM, typename FS>
-__device__ __forceinline__ int draw_target_row(const Params& P, const Req& R, int row, float M, int exclude,
-                               float csx, float tau, double u, FM cm, FS cs, Smem& sm,
-                               DrawShared& ds) {
+// `exclude` = the rejected draft id, zero-residual fallback).  cm(c) gives
+// chunk c's max, mass(c, ex) its mass scaled to the row max (ex: leave the
+// token `exclude` out of x's chunk) and rc(c) that scale, so mass / rc is in
+// units of the chunk's own terms.  Returns the token (all threads).
+template <typename TT, bool AL, typename FM, typename FS, typename FR>
+__device__ __forceinline__ int draw_target_row(const Params& P, const Req& R, int row, int exclude,
+                                               float tau, double u, FM cm, FS mass, FR rc,
+                                               Smem& sm, DrawShared& ds) {
   const int nc = P.nc;
-  const double Mc = (double)M * R.ce;
   for (int attempt = 0; attempt < 2; ++attempt) {
     for (int c = threadIdx.x; c < nc; c += WG) {
-      const float m = cm(c);
-      double e = 0.0;
-      if (m > NEG_INF) {
-        const double R_c = exp2((double)chunk_off(m, R.c32) - Mc);
-        const float sc = (exclude >= 0 && exclude / CHUNK == c) ? csx : cs(c);
-        e = (double)sc * R_c;
-        if (!(e > 0.0)) e = 0.0;
-      }
+      double e = mass(c, exclude >= 0 && exclude / CHUNK == c);
+      if (!(e > 0.0)) e = 0.0;
       ds.E[c] = e;
     }
     if (pick_chunk(nc, u, ds)) break;
@@ -763,17 +898,15 @@ __device__ __forceinline__ int draw_target_row(const Params& P, const Req& R, in
   }
   const int ch = ds.chunk;
   const float m = cm(ch);
-  const double R_c = exp2((double)chunk_off(m, R.c32) - Mc);
-  const double tl = ds.tl / R_c;
-  const float off = chunk_off(m, R.c32);
+  const double tl = ds.tl / rc(ch);
   const int c0 = ch * CHUNK;
   const int n = min(CHUNK, P.vocab - c0);
   const TT* rp = (const TT*)P.target + (int64_t)row * P.ld_t;
   const bool vec_ok = AL;
-  const float c32 = R.c32, clo = R.clo;
+  const float cf = R.c;
   auto wf = [=](float x, float, int e) -> double {
     if (x < tau || e == exclude) x = NEG_INF;
-    return (double)eterm(x, c32, clo, off);
+    return (double)term(x, m, cf);
   };
   return draw_chunk<TT, TT, false>(rp, rp, vec_ok, vec_ok, 0.f, c0, n, tl, wf, sm, ds);
 }
@@ -881,17 +1014,39 @@ __device__ __forceinline__ void finalize(const Params& P, int b, int cu0, int k,
   }
   __syncthreads();
 
+  // row maxima (one thread per staged row: target rows 0..k, draft rows 0..k-1)
+  const bool staged = !R.bad_param && !badtok_any && !fs.timeout;
+  const int nrows = (k + 1) + (logits ? k : 0);
+  if (staged && tid < nrows) {
+    float Mr = NEG_INF;
+    for (int c = 0; c < nc; ++c) Mr = fmax3nan(Mr, st_m[tid * nc + c]);
+    if (tid <= k) fs.M[tid] = Mr;
+    else fs.Mq[tid - k - 1] = Mr;
+  }
+  __syncthreads();
+  // sampled rows: each chunk sum scaled to its row max, in place (all threads)
+  if (staged && sampled) {
+    for (int e = tid; e < nrows * nc; e += WG) {
+      const int slot = e / nc;
+      const float Mr = slot <= k ? fs.M[slot] : fs.Mq[slot - k - 1];
+      const float m = st_m[e];
+      float v = 0.f;
+      if (Mr > NEG_INF && Mr < POS_INF && m > NEG_INF) v = __uint_as_float(st_s[e]) * term(m, Mr, R.c);
+      st_s[e] = __float_as_uint(v);
+    }
+  }
+  __syncthreads();
+
   if (tid < 64) {
     const int j = tid;
     bool nonfin = false, empty = false, acc = false;
     float M = NEG_INF, Mq = NEG_INF;
     double S = 0.0, Sq = 0.0;
     int g = -1;
-    const bool staged = !R.bad_param && !badtok_any && !fs.timeout;
     if (j <= k && staged) {
       const float* mrow = st_m + j * nc;
       const uint32_t* srow = st_s + j * nc;
-      for (int c = 0; c < nc; ++c) M = fmax3nan(M, mrow[c]);
+      M = fs.M[j];
       if (R.greedy) {
         for (int c = 0; c < nc; ++c) {
           if (mrow[c] == M) {
@@ -899,24 +1054,15 @@ __device__ __forceinline__ void finalize(const Params& P, int b, int cu0, int k,
             break;
           }
         }
-      } else if (M > NEG_INF && M < POS_INF) {
-        const double Mc = (double)M * R.ce;
-        for (int c = 0; c < nc; ++c)
-          if (mrow[c] > NEG_INF)
-            S += (double)__uint_as_float(srow[c]) * exp2((double)chunk_off(mrow[c], R.c32) - Mc);
+      } else {
+        for (int c = 0; c < nc; ++c) S += (double)__uint_as_float(srow[c]);
       }
       nonfin = (M != M) || M == POS_INF;
       empty = M == NEG_INF;
       if (logits && j < k) {
-        const float* qm = st_m + (k + 1 + j) * nc;
         const uint32_t* qs = st_s + (k + 1 + j) * nc;
-        for (int c = 0; c < nc; ++c) Mq = fmax3nan(Mq, qm[c]);
-        if (Mq > NEG_INF && Mq < POS_INF) {
-          const double Mc = (double)Mq * R.ce;
-          for (int c = 0; c < nc; ++c)
-            if (qm[c] > NEG_INF)
-              Sq += (double)__uint_as_float(qs[c]) * exp2((double)chunk_off(qm[c], R.c32) - Mc);
-        }
+        Mq = fs.Mq[j];
+        for (int c = 0; c < nc; ++c) Sq += (double)__uint_as_float(qs[c]);
         nonfin = nonfin || (Mq != Mq) || Mq == POS_INF;
         empty = empty || Mq == NEG_INF;
       }
@@ -988,12 +1134,19 @@ __device__ __forceinline__ void finalize(const Params& P, int b, int cu0, int k,
     const int row = cu0 + a;
     const float tau = (P.thr_t && R.filt) ? thr_of(P.thr_t, row) : NEG_INF;
     const int exclude = (a < k) ? fs.x[a] : -1;
+    // st_s holds the chunk sums already scaled to the row max
     const float* mrow = st_m + a * nc;
     const uint32_t* srow = st_s + a * nc;
-    const int t = draw_target_row<TT, AL>(
-        P, R, row, fs.M[a], exclude, exclude >= 0 ? fs.sx[a] : 0.f, tau,
-        (double)P.u[cu0 + k], [=](int c) { return mrow[c]; },
-        [=](int c) { return __uint_as_float(srow[c]); }, sm, ds);
+    const float Ma = fs.M[a];
+    const float sxa = exclude >= 0 ? fs.sx[a] : 0.f;
+    const float cf = R.c;
+    auto rc = [=](int c) { return (double)term(mrow[c], Ma, cf); };
+    auto mass = [=](int c, bool ex) {
+      if (!(mrow[c] > NEG_INF)) return 0.0;
+      return ex ? (double)(sxa * term(mrow[c], Ma, cf)) : (double)__uint_as_float(srow[c]);
+    };
+    const int t = draw_target_row<TT, AL>(P, R, row, exclude, tau, (double)P.u[cu0 + k],
+                                          [=](int c) { return mrow[c]; }, mass, rc, sm, ds);
     if (tid == 0) P.out[row] = t;
     if (has_helpers(P, R)) helpers_none(P, b);
   } else if (mode == 2) {
@@ -1028,7 +1181,7 @@ __device__ __forceinline__ void finalize(const Params& P, int b, int cu0, int k,
 // helpers: residual max(0, p - q) at the first rejection
 // ---------------------------------------------------------------------------
 struct ResCtx {
-  float offp, offq;
+  float mp, mq;    // chunk maxima of target and draft
   double sp, sq;   // per-chunk scale R_c / S of target and draft
   float taup, tauq;
 };
@@ -1038,11 +1191,11 @@ struct ResCtx {
 template <bool LOGITS>
 __device__ __forceinline__ double resid_elem(float lp, float lq, const Req& R, const ResCtx& X) {
   if (lp < X.taup) lp = NEG_INF;
-  const double p = (double)eterm(lp, R.c32, R.clo, X.offp) * X.sp;
+  const double p = (double)term(lp, X.mp, R.c) * X.sp;
   double q;
   if (LOGITS) {
     if (lq < X.tauq) lq = NEG_INF;
-    q = (double)eterm(lq, R.c32, R.clo, X.offq) * X.sq;
+    q = (double)term(lq, X.mq, R.c) * X.sq;
   } else {
     q = (double)lq;
   }
@@ -1052,15 +1205,15 @@ __device__ __forceinline__ double resid_elem(float lp, float lq, const Req& R, c
 
 __device__ __forceinline__ void res_ctx(const Params& P, const Req& R, const Setup& su, float mp,
                                         float mq, int trow, int drow, ResCtx& X) {
-  X.offp = (mp > NEG_INF) ? chunk_off(mp, R.c32) : 0.f;
-  X.sp = (mp > NEG_INF) ? exp2((double)X.offp - (double)su.Mp * R.ce) / su.Sp : 0.0;
+  X.mp = (mp > NEG_INF) ? mp : 0.f;
+  X.sp = (mp > NEG_INF) ? scale_d(mp, su.Mp, R.ce) / su.Sp : 0.0;
   X.taup = (P.thr_t && R.filt) ? thr_of(P.thr_t, trow) : NEG_INF;
-  X.offq = 0.f;
+  X.mq = 0.f;
   X.sq = 0.0;
   X.tauq = NEG_INF;
   if (R.kind == SV_DRAFT_LOGITS) {
-    X.offq = (mq > NEG_INF) ? chunk_off(mq, R.c32) : 0.f;
-    X.sq = (mq > NEG_INF) ? exp2((double)X.offq - (double)su.Mq * R.ce) / su.Sq : 0.0;
+    X.mq = (mq > NEG_INF) ? mq : 0.f;
+    X.sq = (mq > NEG_INF) ? scale_d(mq, su.Mq, R.ce) / su.Sq : 0.0;
     X.tauq = (P.thr_d && R.filt) ? thr_of(P.thr_d, drow) : NEG_INF;
   }
 }
@@ -1185,10 +1338,16 @@ __device__ __forceinline__ void helper(const Params& P, int b, int c, Smem& sm, 
     // row's chunk statistics (their payloads stay in the words after consumption)
     const float tau = (P.thr_t && R.filt) ? thr_of(P.thr_t, trow) : NEG_INF;
     const u64* cw = P.cst + (int64_t)trow * nc * 2;
-    const int t = draw_target_row<TT, AL>(
-        P, R, trow, su.Mp, -1, 0.f, tau, u,
-        [=](int cc) { return __uint_as_float(lo32(ld_agent(cw + 2 * cc))); },
-        [=](int cc) { return __uint_as_float(lo32(ld_agent(cw + 2 * cc + 1))); }, sm, ds);
+    const float Mp = su.Mp;
+    const double ce = R.ce;
+    auto cm = [=](int cc) { return __uint_as_float(lo32(ld_agent(cw + 2 * cc))); };
+    auto rc = [=](int cc) { return scale_d(cm(cc), Mp, ce); };
+    auto mass = [=](int cc, bool) {
+      const float m = cm(cc);
+      if (!(m > NEG_INF)) return 0.0;
+      return (double)__uint_as_float(lo32(ld_agent(cw + 2 * cc + 1))) * scale_d(m, Mp, ce);
+    };
+    const int t = draw_target_row<TT, AL>(P, R, trow, -1, tau, u, cm, mass, rc, sm, ds);
     if (threadIdx.x == 0) P.out[trow] = t;
   } else {
     const int ch = ds.chunk;
@@ -1219,12 +1378,57 @@ __device__ __forceinline__ void helper(const Params& P, int b, int c, Smem& sm, 
 //   producers of request p (p < batch; (max_k+1) * ns workgroups, row-major)
 //   followed by the helpers of request p-1 (p >= 1; H workgroups).
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// launch order of the requests
+// ---------------------------------------------------------------------------
+// Requests are laid out in the grid by class: sampled requests with draft rows
+// (their rejection needs the helpers) first, other sampled requests next,
+// greedy ones last, each class in request order.  The work after a request's
+// last producer (merge, draws, residual) then overlaps later requests'
+// producers, and the call ends on the cheapest chains.
+__device__ __forceinline__ int req_class(const Params& P, int b) {
+  const float T = P.temp[b];
+  if (!(T >= FLT_MIN)) return 2;
+  const int kind = P.kind[b];
+  return (kind == SV_DRAFT_LOGITS || kind == SV_DRAFT_PROBS) ? 0 : 1;
+}
+
+// Request at launch position pos (computed by every wave on its own; uniform).
+__device__ __forceinline__ int req_at(const Params& P, int pos) {
+  if (P.greedy_entry) return pos;
+  const int lane = threadIdx.x & 63;
+  const int B = P.batch;
+  int cl0 = lane < B ? req_class(P, lane) : 3;
+  int n0 = 0, n1 = 0;
+  for (int base = 0; base < B; base += 64) {
+    const int cl = base == 0 ? cl0 : (base + lane < B ? req_class(P, base + lane) : 3);
+    n0 += __popcll(__ballot(cl == 0));
+    n1 += __popcll(__ballot(cl == 1));
+  }
+  const int tc = pos < n0 ? 0 : (pos < n0 + n1 ? 1 : 2);
+  int r = pos - (tc >= 1 ? n0 : 0) - (tc == 2 ? n1 : 0);
+  for (int base = 0; base < B; base += 64) {
+    const int cl = base == 0 ? cl0 : (base + lane < B ? req_class(P, base + lane) : 3);
+    const uint64_t m = __ballot(cl == tc);
+    const int cnt = __popcll(m);
+    if (r < cnt) {
+      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      const uint64_t hit = __ballot(cl == tc && below == r);
+      return base + __builtin_ctzll(hit);
+    }
+    r -= cnt;
+  }
+  return pos;   // not reached: the classes partition the batch
+}
+
 template <typename TT, typename TD, bool AL>
 __global__ __launch_bounds__(WG) void k_verify(const Params P) {
   __shared__ Smem sm;
   __shared__ FinShared fs;
   __shared__ DrawShared ds;
   __shared__ HelpShared hs;
+  __shared__ ProdShared ps;
   extern __shared__ uint32_t stage[];
   const int Pw = (P.max_k + 1) * P.ns;
   const int H = P.H;
@@ -1245,11 +1449,11 @@ __global__ __launch_bounds__(WG) void k_verify(const Params P) {
       loc = Pw + (rest - mid);
     }
   }
-  if (loc >= Pw) {   // helper of request per-1, chunk loc-Pw
-    helper<TT, TD, AL>(P, (int)per - 1, (int)(loc - Pw), sm, ds, hs);
+  if (loc >= Pw) {   // helper of the request at position per-1, chunk loc-Pw
+    helper<TT, TD, AL>(P, req_at(P, (int)per - 1), (int)(loc - Pw), sm, ds, hs);
     return;
   }
-  const int b = (int)per;
+  const int b = req_at(P, (int)per);
   const int j = (int)(loc / P.ns);
   const int s = (int)(loc % P.ns);
   const int cu0 = P.cu[b];
@@ -1263,8 +1467,12 @@ __global__ __launch_bounds__(WG) void k_verify(const Params P) {
     return;
   }
   if (j > k) return;
+  // the strip's first chunk is requested before the request's parameters
+  Buf<TT, TD> A;
+  issue_task<TT, TD, AL>((const TT*)P.target + (int64_t)(cu0 + j) * P.ld_t, (const TD*)nullptr,
+                         false, s * P.S, P.vocab, A);
   const Req R = load_req(P, b);
-  if (!R.bad_param) produce<TT, TD, AL>(P, R, b, cu0, k, j, s, sm);
+  if (!R.bad_param) produce<TT, TD, AL>(P, R, b, cu0, k, j, s, ps, A);
   if (j == k && s == P.ns - 1) finalize<TT, TD, AL>(P, b, cu0, k, R, sm, fs, ds, stage);
 }
 
@@ -1347,7 +1555,6 @@ __device__ float row_threshold(const T* __restrict__ rp, int V, int levels, cons
   }
   if (do_p) {
     const float tau_k = do_k ? keyf(tau_key) : NEG_INF;
-    const float off = chunk_off(M, R.c32);
     uint32_t prefix = 0u, pmask = 0u;
     double target = 0.0;
     for (int lev = 0; lev < levels; ++lev) {
@@ -1360,7 +1567,7 @@ __device__ float row_threshold(const T* __restrict__ rp, int V, int levels, cons
         const uint32_t key = fkey(v);
         if ((key & pmask) != prefix) continue;
         const unsigned long long fx =
-            (unsigned long long)__double2ll_rn((double)eterm(v, R.c32, R.clo, off) * FIX);
+            (unsigned long long)__double2ll_rn((double)term(v, M, R.c) * FIX);
         atomicAdd(&th.mass[w][(key >> shift) & 255u], fx);
       }
       __syncthreads();
@@ -1470,7 +1677,7 @@ static long long verify_grid(const Params& P) {
 
 template <typename TT, typename TD>
 static int launch_all(Params P, bool sampled, bool filters, bool aligned, hipStream_t st) {
-  P.S = Strip<TT>::S;
+  P.S = Strip<TT>::S;   // at most 8: a strip's statistics fit ProdShared::pub
   P.ns = (P.nc + P.S - 1) / P.S;
   P.H = sampled ? P.nc : 0;
   const long long g = verify_grid<TT>(P);
