@@ -326,6 +326,15 @@ def test_status_codes():
                       np.zeros(11, np.float32), np.ones(1, np.float32),
                       draft_kind=np.array([ONEHOT]), max_k=8)
     assert r.status[0] == oracle.ROW_BAD_K and r.accepted[0] == -1
+    # offsets that go back: request 1 starts below request 0's first offset
+    # (its rows would overlap request 0's), request 2 is ordered again
+    # (request 2 alone would pass every other check)
+    cu = np.array([0, 3, 2, 6], dtype=np.int32)
+    r = oracle.verify(np.zeros((6, 5), np.float32), F32, cu, np.zeros(3, np.int32),
+                      np.zeros(6, np.float32), np.ones(3, np.float32),
+                      draft_kind=np.array([ONEHOT] * 3), max_k=8)
+    assert list(r.status) == [oracle.ROW_OK, oracle.ROW_BAD_K, oracle.ROW_BAD_K]
+    assert oracle.request_bounds(np.array([0, 2, 6]), 1, 2, 6, 8)[1]
 
 
 def test_greedy_temperature_rule():
