@@ -50,6 +50,9 @@
 #include <float.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <cmath>
+
 #include "specverify.h"
 
 namespace sv {
@@ -60,6 +63,12 @@ constexpr int CHUNK = 8192;
 constexpr int EPT = CHUNK / WG;   // elements per thread per chunk
 constexpr int MAX_NC = 512;       // chunks per row (vocab <= 4,194,304)
 constexpr int MAX_K = 63;         // k+1 positions fit one wave
+// Bytes streamed between a request's producers and its helpers (about the time
+// its finalizer needs to decide).
+#ifndef SV_HELPER_DELAY_MB
+#define SV_HELPER_DELAY_MB 64
+#endif
+constexpr double HELPER_DELAY_BYTES = SV_HELPER_DELAY_MB * 1048576.0;
 constexpr int STAGE_MAX = 49152;  // bytes of LDS the finalizer may stage statistics in
 constexpr int SPIN_MAX = 1 << 18; // polls before a wait gives up
 constexpr float NEG_INF = -__builtin_inff();
@@ -111,6 +120,7 @@ struct Params {
   int S;          // chunks per producer strip
   int ns;         // strips per row
   int H;          // helper workgroups per request (nc, or 0 for the greedy entry)
+  int dwg;        // periods between a request's producers and its helpers
   int greedy_entry;
 };
 
@@ -202,7 +212,15 @@ __device__ __forceinline__ uint4 load_word_scalar(const T* __restrict__ cp, int 
 // row's pitch); finish_words then masks the tail past n.  issue_words returns
 // without waiting for the data, so a chunk's loads can be in flight while the
 // previous chunk is reduced.
-template <typename T, typename OF>
+// One 128-bit word loaded without keeping it in the caches (rows the producers
+// read once).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream(const void* p) {
+  const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+template <typename T, typename OF, bool NT = false>
 __device__ __forceinline__ void issue_words(const T* __restrict__ cp, int n, bool al, float fill,
                                             OF offs, Seg<T>& s) {
   constexpr int VEC = VT<T>::VEC;
@@ -210,7 +228,8 @@ __device__ __forceinline__ void issue_words(const T* __restrict__ cp, int n, boo
     const int last = ((n - 1) / VEC) * VEC;
 #pragma unroll
     for (int i = 0; i < Seg<T>::NV; ++i)
-      s.q[i] = *reinterpret_cast<const uint4*>(cp + min(offs(i), last));
+      s.q[i] = NT ? ld_stream(cp + min(offs(i), last))
+                  : *reinterpret_cast<const uint4*>(cp + min(offs(i), last));
   } else {
 #pragma unroll
     for (int i = 0; i < Seg<T>::NV; ++i) s.q[i] = load_word_scalar<T>(cp, offs(i), n, fill);
@@ -641,8 +660,11 @@ __device__ __forceinline__ CStat chunk_stats(Seg<T>& sg, bool greedy, float tau,
 
 // chunks per producer strip (64 KiB of bf16 or fp32 target data)
 template <typename TT> struct Strip;
-template <> struct Strip<uint16_t> { static constexpr int S = 4; };
-template <> struct Strip<float> { static constexpr int S = 2; };
+#ifndef SV_STRIP_BF16
+#define SV_STRIP_BF16 4
+#endif
+template <> struct Strip<uint16_t> { static constexpr int S = SV_STRIP_BF16; };
+template <> struct Strip<float> { static constexpr int S = (SV_STRIP_BF16 + 1) / 2; };
 static_assert(Strip<uint16_t>::S <= 8 && Strip<float>::S <= 8, "strip too long");
 
 // Words of one chunk of either element type (sized for the wider one).
@@ -656,7 +678,8 @@ template <typename T, typename TT, typename TD>
 __device__ __forceinline__ void buf_issue(const T* __restrict__ cp, int n, bool al,
                                           Buf<TT, TD>& b) {
   Seg<T> sg;
-  issue_words<T>(cp, n, al, NEG_INF, [](int i) { return strided_off<T>(i); }, sg);
+  auto offs = [](int i) { return strided_off<T>(i); };
+  issue_words<T, decltype(offs), true>(cp, n, al, NEG_INF, offs, sg);
 #pragma unroll
   for (int i = 0; i < Seg<T>::NV; ++i) b.q[i] = sg.q[i];
 }
@@ -1224,12 +1247,9 @@ struct HelpShared {
 };
 
 template <typename TT, typename TD, bool AL>
-__device__ __forceinline__ void helper(const Params& P, int b, int c, Smem& sm, DrawShared& ds, HelpShared& hs) {
+__device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, int c, Smem& sm,
+                                       DrawShared& ds, HelpShared& hs) {
   const int nc = P.nc;
-  const int cu0 = P.cu[b];
-  const int cu1 = P.cu[b + 1];
-  const int k = cu1 - cu0 - 1;
-  if (!req_valid(P, b, cu0, cu1, k)) return;
   const Req R = load_req(P, b);
   if (!has_helpers(P, R)) return;
   const bool logits = R.kind == SV_DRAFT_LOGITS;
@@ -1374,9 +1394,14 @@ __device__ __forceinline__ void helper(const Params& P, int b, int c, Smem& sm, 
 
 // ---------------------------------------------------------------------------
 // k_verify: block index -> role
-//   The launch is a sequence of periods p = 0 .. batch: period p holds the
-//   producers of request p (p < batch; (max_k+1) * ns workgroups, row-major)
-//   followed by the helpers of request p-1 (p >= 1; H workgroups).
+//   The launch is a sequence of periods p = 0, 1, ...: period p holds the
+//   producers of the request at launch position p ((max_k+1) * ns workgroups,
+//   row j, strip s; p < batch), then the helpers of the request at position
+//   p - D (H workgroups; 0 <= p - D < batch).  The D periods between a
+//   request's producers and its helpers give its finalizer the time to decide
+//   (the host sizes D from the bytes the periods stream), and the sampled
+//   requests with draft rows -- the only ones whose helpers have work -- come
+//   first, so their residual draws run while later requests still stream.
 // ---------------------------------------------------------------------------
 // ---------------------------------------------------------------------------
 // launch order of the requests
@@ -1384,45 +1409,118 @@ __device__ __forceinline__ void helper(const Params& P, int b, int c, Smem& sm, 
 // Requests are laid out in the grid by class: sampled requests with draft rows
 // (their rejection needs the helpers) first, other sampled requests next,
 // greedy ones last, each class in request order.  The work after a request's
-// last producer (merge, draws, residual) then overlaps later requests'
-// producers, and the call ends on the cheapest chains.
-__device__ __forceinline__ int req_class(const Params& P, int b) {
-  const float T = P.temp[b];
-  if (!(T >= FLT_MIN)) return 2;
-  const int kind = P.kind[b];
-  return (kind == SV_DRAFT_LOGITS || kind == SV_DRAFT_PROBS) ? 0 : 1;
+// last producer (merge, draws) then overlaps later requests' producers, and
+// the call ends on the cheapest chains.
+//
+// Every wave finds the request at its launch position on its own: E
+// consecutive requests per lane (E = 1 for batches of up to 64, else 16),
+// their offsets, temperatures and draft kinds loaded together (one round trip,
+// indices clamped into the batch), classes counted by ballots and DPP scans.
+// A request is valid when its offsets pass req_valid and its first offset is
+// not below any earlier one (the rows of valid requests never overlap).
+struct ReqPos {
+  int b, cu0, cu1;
+  bool valid;
+};
+
+__device__ __forceinline__ int wave_scan_add(int x) {   // inclusive, over the wave
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return x;
+}
+__device__ __forceinline__ int wave_scan_max(int x) {   // inclusive, over the wave
+  x = max(x, __builtin_amdgcn_update_dpp(INT32_MIN, x, 0x111, 0xf, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(INT32_MIN, x, 0x112, 0xf, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(INT32_MIN, x, 0x114, 0xf, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(INT32_MIN, x, 0x118, 0xf, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(INT32_MIN, x, 0x142, 0xa, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(INT32_MIN, x, 0x143, 0xc, 0xf, false));
+  return x;
 }
 
-// Request at launch position pos (computed by every wave on its own; uniform).
-__device__ __forceinline__ int req_at(const Params& P, int pos) {
-  if (P.greedy_entry) return pos;
+template <int E>
+__device__ __forceinline__ ReqPos req_at(const Params& P, int pos) {
   const int lane = threadIdx.x & 63;
   const int B = P.batch;
-  int cl0 = lane < B ? req_class(P, lane) : 3;
-  int n0 = 0, n1 = 0;
-  for (int base = 0; base < B; base += 64) {
-    const int cl = base == 0 ? cl0 : (base + lane < B ? req_class(P, base + lane) : 3);
-    n0 += __popcll(__ballot(cl == 0));
-    n1 += __popcll(__ballot(cl == 1));
-  }
-  const int tc = pos < n0 ? 0 : (pos < n0 + n1 ? 1 : 2);
-  int r = pos - (tc >= 1 ? n0 : 0) - (tc == 2 ? n1 : 0);
-  for (int base = 0; base < B; base += 64) {
-    const int cl = base == 0 ? cl0 : (base + lane < B ? req_class(P, base + lane) : 3);
-    const uint64_t m = __ballot(cl == tc);
-    const int cnt = __popcll(m);
-    if (r < cnt) {
-      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      const uint64_t hit = __ballot(cl == tc && below == r);
-      return base + __builtin_ctzll(hit);
+  const int i0 = lane * E;
+  int lo[E + 1], cl[E];
+#pragma unroll
+  for (int e = 0; e <= E; ++e) lo[e] = P.cu[min(i0 + e, B)];
+  if (!P.greedy_entry) {
+    float T[E];
+    int kd[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int i = min(i0 + e, B - 1);
+      T[e] = P.temp[i];
+      kd[e] = P.kind[i];
     }
-    r -= cnt;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      cl[e] = (i0 + e >= B) ? 3 : !(T[e] >= FLT_MIN) ? 2
+              : (kd[e] == SV_DRAFT_LOGITS || kd[e] == SV_DRAFT_PROBS) ? 0 : 1;
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) cl[e] = (i0 + e >= B) ? 3 : 2;
   }
-  return pos;   // not reached: the classes partition the batch
+  // class counts: totals and this lane's exclusive prefix
+  int c0 = 0, c1 = 0, c2 = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    c0 += cl[e] == 0;
+    c1 += cl[e] == 1;
+    c2 += cl[e] == 2;
+  }
+  const int s0 = wave_scan_add(c0), s1 = wave_scan_add(c1), s2 = wave_scan_add(c2);
+  const int n0 = __builtin_amdgcn_readlane(s0, 63), n1 = __builtin_amdgcn_readlane(s1, 63);
+  const int tc = pos < n0 ? 0 : (pos < n0 + n1 ? 1 : 2);
+  const int r = pos - (tc >= 1 ? n0 : 0) - (tc == 2 ? n1 : 0);
+  const int cnt = tc == 0 ? c0 : (tc == 1 ? c1 : c2);
+  const int excl = (tc == 0 ? s0 : (tc == 1 ? s1 : s2)) - cnt;
+  const bool mine = r >= excl && r < excl + cnt;
+  // the lane's entry of rank r within class tc
+  int ei = 0, seen = excl;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (cl[e] == tc) {
+      if (seen == r) ei = e;
+      ++seen;
+    }
+  }
+  // offsets must not go back: the running max of cu[0..i-1] at that entry
+  int mloc = INT32_MIN, run_at = INT32_MIN;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (e == ei) run_at = mloc;
+    mloc = (i0 + e < B) ? max(mloc, lo[e]) : mloc;
+  }
+  const int minc = wave_scan_max(mloc);
+  const int before = __builtin_amdgcn_update_dpp(INT32_MIN, minc, 0x138, 0xf, 0xf, false);  // wave_shr:1
+  run_at = max(run_at, before);
+  int c_lo = 0, c_hi = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (e == ei) {
+      c_lo = lo[e];
+      c_hi = lo[e + 1];
+    }
+  }
+  const uint64_t m = __ballot(mine);
+  const int src = m ? (int)__builtin_ctzll(m) : 0;   // classes partition the batch: m != 0
+  ReqPos R;
+  R.b = __builtin_amdgcn_readlane(i0 + ei, src);
+  R.cu0 = __builtin_amdgcn_readlane(c_lo, src);
+  R.cu1 = __builtin_amdgcn_readlane(c_hi, src);
+  const int ra = __builtin_amdgcn_readlane(run_at, src);
+  R.valid = R.cu0 >= ra && req_valid(P, R.b, R.cu0, R.cu1, R.cu1 - R.cu0 - 1);
+  return R;
 }
 
-template <typename TT, typename TD, bool AL>
+template <typename TT, typename TD, bool AL, int E>
 __global__ __launch_bounds__(WG) void k_verify(const Params P) {
   __shared__ Smem sm;
   __shared__ FinShared fs;
@@ -1432,34 +1530,38 @@ __global__ __launch_bounds__(WG) void k_verify(const Params P) {
   extern __shared__ uint32_t stage[];
   const int Pw = (P.max_k + 1) * P.ns;
   const int H = P.H;
+  const int Dp = H > 0 ? min(P.dwg, P.batch) : P.batch;
   const long long id = blockIdx.x;
-  long long per, loc;
-  if (id < Pw) {
-    per = 0;
-    loc = id;
-  } else {
-    const long long rest = id - Pw;
-    const long long span = (long long)Pw + H;
-    const long long mid = (long long)(P.batch - 1) * span;
-    if (rest < mid) {
-      per = 1 + rest / span;
-      loc = rest % span;
-    } else {
-      per = P.batch;
-      loc = Pw + (rest - mid);
-    }
+  const long long seg1 = (long long)Dp * Pw;                       // periods 0 .. Dp-1
+  const long long seg2 = (long long)(P.batch - Dp) * (Pw + H);     // periods Dp .. batch-1
+  int per, loc, hpos = -1;
+  if (id < seg1) {
+    per = (int)(id / Pw);
+    loc = (int)(id - (long long)per * Pw);
+  } else if (id < seg1 + seg2) {
+    const long long rest = id - seg1;
+    const int q = (int)(rest / (Pw + H));
+    per = Dp + q;
+    loc = (int)(rest - (long long)q * (Pw + H));
+    if (loc >= Pw) hpos = per - Dp;
+  } else {                                                         // helpers of the last Dp positions
+    const long long rest = id - seg1 - seg2;
+    per = P.batch;
+    hpos = P.batch - Dp + (int)(rest / H);
+    loc = Pw + (int)(rest % H);
   }
-  if (loc >= Pw) {   // helper of the request at position per-1, chunk loc-Pw
-    helper<TT, TD, AL>(P, req_at(P, (int)per - 1), (int)(loc - Pw), sm, ds, hs);
+  if (hpos >= 0) {   // helper of the request at position hpos, chunk loc - Pw
+    const ReqPos Q = req_at<E>(P, hpos);
+    if (Q.valid) helper<TT, TD, AL>(P, Q.b, Q.cu0, Q.cu1 - Q.cu0 - 1, loc - Pw, sm, ds, hs);
     return;
   }
-  const int b = req_at(P, (int)per);
-  const int j = (int)(loc / P.ns);
-  const int s = (int)(loc % P.ns);
-  const int cu0 = P.cu[b];
-  const int cu1 = P.cu[b + 1];
-  const int k = cu1 - cu0 - 1;
-  if (!req_valid(P, b, cu0, cu1, k)) {
+  const int j = loc / P.ns;
+  const int s = loc - j * P.ns;
+  const ReqPos Q = req_at<E>(P, per);
+  const int b = Q.b;
+  const int cu0 = Q.cu0;
+  const int k = Q.cu1 - cu0 - 1;
+  if (!Q.valid) {
     if (j == 0 && s == 0 && threadIdx.x == 0) {
       P.accepted[b] = -1;
       P.status[b] = SV_ROW_BAD_K;
@@ -1678,6 +1780,11 @@ static long long verify_grid(const Params& P) {
 template <typename TT, typename TD>
 static int launch_all(Params P, bool sampled, bool filters, bool aligned, hipStream_t st) {
   P.S = Strip<TT>::S;   // at most 8: a strip's statistics fit ProdShared::pub
+  {
+    // helper delay: the periods streaming about HELPER_DELAY_BYTES
+    const double per_bytes = (double)P.total_rows / P.batch * P.vocab * sizeof(TT);
+    P.dwg = (int)std::min<double>(P.batch, std::max(1.0, std::ceil(HELPER_DELAY_BYTES / per_bytes)));
+  }
   P.ns = (P.nc + P.S - 1) / P.S;
   P.H = sampled ? P.nc : 0;
   const long long g = verify_grid<TT>(P);
@@ -1687,10 +1794,18 @@ static int launch_all(Params P, bool sampled, bool filters, bool aligned, hipStr
     const long long g0 = (long long)P.batch * (P.max_k + 1) * 2;
     hipLaunchKernelGGL((k_thresh<TT, TD>), dim3((unsigned)g0), dim3(WG), 0, st, P);
   }
-  if (aligned)
-    hipLaunchKernelGGL((k_verify<TT, TD, true>), dim3((unsigned)g), dim3(WG), lds, st, P);
-  else
-    hipLaunchKernelGGL((k_verify<TT, TD, false>), dim3((unsigned)g), dim3(WG), lds, st, P);
+  // requests per lane when finding a request by launch position
+  if (P.batch <= 64) {
+    if (aligned)
+      hipLaunchKernelGGL((k_verify<TT, TD, true, 1>), dim3((unsigned)g), dim3(WG), lds, st, P);
+    else
+      hipLaunchKernelGGL((k_verify<TT, TD, false, 1>), dim3((unsigned)g), dim3(WG), lds, st, P);
+  } else {
+    if (aligned)
+      hipLaunchKernelGGL((k_verify<TT, TD, true, 16>), dim3((unsigned)g), dim3(WG), lds, st, P);
+    else
+      hipLaunchKernelGGL((k_verify<TT, TD, false, 16>), dim3((unsigned)g), dim3(WG), lds, st, P);
+  }
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }
 
@@ -1713,10 +1828,12 @@ static int dispatch(const Params& P, int tdt, int ddt, bool sampled, bool filter
   return launch_all<uint16_t, uint16_t>(P, sampled, filters, al, st);
 }
 
+constexpr int MAX_BATCH = 64 * 16;   // requests a wave finds its request among
+
 static bool grid_ok(int batch, int max_k, int nc) {
   // strips of one chunk are the worst case
   const long long g = (long long)batch * (max_k + 1) * nc + (long long)batch * nc;
-  return g < (1LL << 31);
+  return batch <= MAX_BATCH && g < (1LL << 31);
 }
 
 static void carve(Params& P, void* ws, const Layout& L) {

@@ -310,3 +310,15 @@ def test_workspace_reuse_across_shapes():
     and vocab on the same cached workspace)."""
     for B, V in ((32, 30000), (5, 9000), (40, 17000), (5, 9000)):
         check(synth.make(2, seed=B, batch=B, vocab=V))
+
+
+def test_offsets_going_back():
+    """A request whose first offset is below an earlier offset is BAD_K on
+    both sides (its rows would overlap an earlier request's)."""
+    w = synth.make(2, seed=3, batch=6, vocab=9000)
+    cu = w.cu_seqlens.copy()
+    cu[3] = cu[1]          # request 2: negative k; request 3 starts inside request 0..1
+    w.cu_seqlens = cu
+    gpu, counts = check(w)
+    assert counts["status"] >= 2
+    assert int(gpu["status"][2]) == oracle.ROW_BAD_K and int(gpu["status"][3]) == oracle.ROW_BAD_K
