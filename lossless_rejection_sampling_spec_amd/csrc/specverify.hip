@@ -397,6 +397,14 @@ __device__ __forceinline__ void block_scan_d(double own, double& excl, double& i
   excl = (lane == 0) ? carry : prev;
 }
 
+// A read-only input at an address that is the same in every lane, loaded
+// through the scalar cache: its wait counter is not the one of the vector
+// loads, so waiting for it never waits for the row data in flight.
+template <typename T>
+__device__ __forceinline__ T ldu(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
 // ---------------------------------------------------------------------------
 // per-request parameters
 // ---------------------------------------------------------------------------
@@ -414,14 +422,14 @@ struct Req {
 
 __device__ __forceinline__ Req load_req(const Params& P, int b) {
   Req R;
-  R.T = P.greedy_entry ? 0.f : P.temp[b];
+  R.T = P.greedy_entry ? 0.f : ldu(P.temp + b);
   R.greedy = P.greedy_entry || !(R.T >= FLT_MIN);
-  R.kind = R.greedy ? -1 : P.kind[b];
+  R.kind = R.greedy ? -1 : ldu(P.kind + b);
   R.bad_param = !R.greedy &&
                 (R.T == POS_INF || R.kind < SV_DRAFT_ONEHOT || R.kind > SV_DRAFT_PROBS ||
                  (R.kind != SV_DRAFT_ONEHOT && P.draft == nullptr));
-  R.K = (!R.greedy && P.top_k) ? P.top_k[b] : 0;
-  R.P = (!R.greedy && P.top_p) ? P.top_p[b] : 1.f;
+  R.K = (!R.greedy && P.top_k) ? ldu(P.top_k + b) : 0;
+  R.P = (!R.greedy && P.top_p) ? ldu(P.top_p + b) : 1.f;
   if (R.K >= P.vocab) R.K = 0;
   R.filt = R.K > 0 || (R.P > 0.f && R.P < 1.f);
   if (!R.greedy && !R.bad_param) {
@@ -440,7 +448,7 @@ __device__ __forceinline__ bool req_valid(const Params& P, int b, int cu0, int c
 }
 
 __device__ __forceinline__ float thr_of(const u64* t, int i) {
-  return __uint_as_float((uint32_t)t[i]);
+  return __uint_as_float((uint32_t)ldu(t + i));
 }
 
 // exp2((v - r) * c) for v <= r, r finite (v = -inf gives 0)
@@ -731,7 +739,7 @@ __device__ __forceinline__ void produce(const Params& P, const Req& R, int b, in
   const bool has_d = R.kind == SV_DRAFT_LOGITS && j < k;
   const TD* drow = (const TD*)P.draft + (int64_t)(d0 + j) * P.ld_d;
   const float taud = (has_d && P.thr_d && R.filt) ? thr_of(P.thr_d, d0 + j) : NEG_INF;
-  const int x = (!R.greedy && j < k) ? P.drafts[d0 + j] : -1;
+  const int x = (!R.greedy && j < k) ? ldu(P.drafts + d0 + j) : -1;
   const int c_begin = s * P.S;
   const int c_end = min(c_begin + P.S, nc);
   const int sh = has_d ? 1 : 0;   // task t: chunk c_begin + (t >> sh), draft iff t & sh
@@ -746,6 +754,20 @@ __device__ __forceinline__ void produce(const Params& P, const Req& R, int b, in
     if (R.kind != SV_DRAFT_ONEHOT) ldx_raw = drow[x];
   }
 
+  if (!has_d) {
+    // target chunks only: every chunk of the strip is requested at once (the
+    // strip's bytes are in flight together), then reduced in order; past the
+    // row's last chunk the loads repeat it (never reduced)
+    constexpr int S = Strip<TT>::S;
+    Buf<TT, TD> Q[S];
+    Q[0] = A;
+#pragma unroll
+    for (int t = 1; t < S; ++t)
+      issue_task<TT, TD, AL>(trow, drow, false, c_begin + min(t, nt - 1), P.vocab, Q[t]);
+#pragma unroll
+    for (int t = 0; t < S; ++t)
+      if (t < nt) produce_task<TT, TT, TD, AL>(P, R, Q[t], false, c_begin + t, x, tau, t, ps);
+  } else {
   Buf<TT, TD> B;   // A holds the first task's loads (issued by the caller)
   int t = 0;
   for (; t + 1 < nt; t += 2) {
@@ -764,6 +786,7 @@ __device__ __forceinline__ void produce(const Params& P, const Req& R, int b, in
   }
   if (t < nt) {   // odd count: the last task is a target chunk, already in A
     produce_task<TT, TT, TD, AL>(P, R, A, false, c_begin + (t >> sh), x, tau, t, ps);
+  }
   }
   __syncthreads();
   const int tp = threadIdx.x;
