@@ -36,14 +36,17 @@
  *   - target rows   cu[b] .. cu[b] + k_b          (row j scores position j)
  *   - draft rows and draft tokens  cu[b]-b .. cu[b]-b+k_b-1
  *   - uniforms u[cu[b] + i]: i < k_b acceptance draws, i = k_b the final draw
- *   total_rows = cu[batch]; cu must be non-decreasing with cu[0] = 0.
+ *   total_rows = cu[batch]; cu must be non-decreasing with cu[0] = 0 (a request
+ *   whose first offset is below an earlier one is reported BAD_K, so the rows
+ *   of the requests that are verified never overlap).
  * Layouts: logit / probability buffers are row-major [rows, ld] with ld >= vocab
  *   elements; only the first `vocab` entries of a row are read.  Rows whose
  *   address is 16-byte aligned take 128-bit loads, others a scalar path.
  * Values: -inf in a logit row masks that token.  NaN or +inf in a needed logit
  *   row, or a NaN/inf/negative needed probability, is a data fault.
  * Per-request status (status[b]) is written on the device; first match wins:
- *   SV_ROW_BAD_K     offsets out of range, k_b < 0 or k_b > max_k
+ *   SV_ROW_BAD_K     offsets out of range, k_b < 0, k_b > max_k, or cu[b] below
+ *                    an earlier offset
  *   SV_ROW_BAD_PARAM unknown draft kind, a kind that needs draft rows with a
  *                    NULL draft buffer, or temperature +inf
  *   SV_ROW_BAD_TOKEN a draft id outside [0, vocab)
@@ -77,9 +80,10 @@ extern "C" {
 enum {
   SV_OK = 0,
   SV_ERR_NULL = 1,      /* a required pointer is NULL */
-  SV_ERR_SHAPE = 2,     /* batch < 1, total_rows < batch, max_k outside [0,63],
-                           vocab < 1 or > 4194304, ld < vocab, (2*max_k+1) *
-                           ceil(vocab/8192) > 6144, or the grid would be too large */
+  SV_ERR_SHAPE = 2,     /* batch < 1 or > 1024, total_rows < batch, max_k outside
+                           [0,63], vocab < 1 or > 4194304, ld < vocab,
+                           (2*max_k+1) * ceil(vocab/8192) > 6144, or the grid
+                           would be too large */
   SV_ERR_DTYPE = 3,     /* unknown dtype code */
   SV_ERR_WORKSPACE = 4, /* workspace_bytes smaller than required */
   SV_ERR_LAUNCH = 5     /* the HIP runtime refused a launch */

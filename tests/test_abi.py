@@ -91,6 +91,8 @@ def test_sampled_shapes_and_dtypes():
     assert _sampled(draft=FAKE, ldd=100, ddt=7) == 3
     assert _sampled(wsb=10) == 4
     assert _sampled(batch=1 << 20, rows=1 << 20, max_k=63, vocab=8192 * 100) == 2
+    assert _sampled(batch=1025, rows=3000) == 2      # more requests than a launch schedules
+    assert _greedy(batch=1025, rows=3000) == 2
 
 
 def test_greedy_validation():
