@@ -77,19 +77,20 @@ constexpr double LOG2E = 1.4426950408889634;
 constexpr uint32_t TAG = 0x80000000u;     // "fresh" bit of a hand-off word (high half)
 constexpr uint32_t F_NONE = 0x40000000u;  // helper decision: no residual to compute
 constexpr uint32_t F_BAD = 0x20000000u;   // residual chunk saw an invalid probability
+// Words of one helper's decision record: 0 the target chunk max (the stop
+// position a in the flag bits), 1 the draft chunk max, 2-3 and 4-5 the fp64
+// target and draft normalizers, 6-7 the target and draft row maxima.
+constexpr int DEC_W = 8;
 
 typedef unsigned long long u64;
 
-// Residual hand-off of one request (plain data).  Every 32-bit value sits in
-// the low half of a 64-bit word, so no word of the workspace ever has its top
-// ("fresh") bit set unless it is a hand-off word in flight.
+// What a helper learns from its decision record (plain data).  Every 32-bit
+// value of the workspace sits in the low half of a 64-bit word, so no word ever
+// has its top ("fresh") bit set unless it is a hand-off word in flight.
 struct Setup {
   double Sp, Sq;
   float Mp, Mq;
   int a;
-};
-struct alignas(16) SetupWords {
-  u64 w[8];   // Sp lo/hi, Sq lo/hi, Mp, Mq, a, (unused)
 };
 
 struct Params {
@@ -110,8 +111,7 @@ struct Params {
   u64* cst;       // [rows][nc][2]  target chunk max / (sum or argmax)
   u64* dst;       // [draft rows][nc][2]
   u64* rx;        // [rows][3]      values at the draft id: l_x, e_x, draft l_x or q(x)
-  SetupWords* setup;  // [batch]
-  u64* dec;       // [batch][nc][2] helper decisions (target / draft chunk max of row a)
+  u64* dec;       // [batch][nc][DEC_W] helper decision records
   u64* res;       // [batch][nc]    residual mass per chunk
   u64* thr_t;     // NULL when no request filters; float bits in the low half
   u64* thr_d;
@@ -305,13 +305,6 @@ __device__ __forceinline__ u64 take_w(u64* w) {
   return 0ull;
 }
 
-// Make this thread's earlier agent-scope stores complete before the ones that
-// follow (used once per request, before its helpers' decision words).
-__device__ __forceinline__ void stores_complete() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_s_waitcnt(0);
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
 
 // ---------------------------------------------------------------------------
 // block reductions (fixed order: deterministic)
@@ -818,6 +811,7 @@ __device__ __forceinline__ void produce(const Params& P, const Req& R, int b, in
 // ---------------------------------------------------------------------------
 struct DrawShared {
   double E[MAX_NC];
+  float va[EPT], vb[EPT];   // the winning thread's elements (rows A and B)
   double tl;
   double wexcl;
   int chunk;
@@ -829,10 +823,10 @@ struct DrawShared {
 // Inverse CDF inside one chunk [c0, c0+n) of a row, in token order.  Thread
 // tid owns the segment [c0 + tid*EPT, c0 + tid*EPT + EPT).  weight(a, b, e)
 // gives the fp64 weight of element e from its values a (row A) and b (row B,
-// only when TWO); it is evaluated again, on the same inputs, when the
-// segment that holds the target is searched.  Returns the first element whose
-// running sum exceeds tl (the last positive element when rounding leaves
-// none).
+// only when TWO); it is evaluated again, on the same inputs (handed to wave 0
+// through LDS by the thread that holds them), when the segment that holds the
+// target is searched.  Returns the first element whose running sum exceeds tl
+// (the last positive element when rounding leaves none).
 template <typename TA, typename TB, bool TWO, typename WF>
 __device__ __forceinline__ int draw_chunk(const TA* __restrict__ pa, const TB* __restrict__ pb, bool avec,
                           bool bvec, float bfill, int c0, int n, double tl, WF weight, Smem& sm,
@@ -841,18 +835,16 @@ __device__ __forceinline__ int draw_chunk(const TA* __restrict__ pa, const TB* _
   const int seg = tid * EPT;               // offset of this thread's segment in the chunk
   double own = 0.0;
   int last_pos = -1;
-  {
-    Seg<TA> sa;
-    Seg<TB> sb;
-    load_contig<TA>(pa + c0, n, avec, NEG_INF, sa);
-    if (TWO) load_contig<TB>(pb + c0, n, bvec, bfill, sb);
+  Seg<TA> sa;
+  Seg<TB> sb;
+  load_contig<TA>(pa + c0, n, avec, NEG_INF, sa);
+  if (TWO) load_contig<TB>(pb + c0, n, bvec, bfill, sb);
 #pragma unroll
-    for (int i = 0; i < EPT; ++i) {
-      const double w = weight(sa.at(i), TWO ? sb.at(i) : 0.f, c0 + seg + i);
-      own += w;
-      last_pos = (w > 0.0) ? c0 + seg + i : last_pos;
-      if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound live fp64 temporaries
-    }
+  for (int i = 0; i < EPT; ++i) {
+    const double w = weight(sa.at(i), TWO ? sb.at(i) : 0.f, c0 + seg + i);
+    own += w;
+    last_pos = (w > 0.0) ? c0 + seg + i : last_pos;
+    if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound live fp64 temporaries
   }
   double excl, incl;
   block_scan_d(own, excl, incl, sm);
@@ -862,6 +854,11 @@ __device__ __forceinline__ int draw_chunk(const TA* __restrict__ pa, const TB* _
     ds.win = tid;
     ds.wexcl = excl;
     ds.wlast = last_pos;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      ds.va[i] = sa.at(i);
+      ds.vb[i] = TWO ? sb.at(i) : bfill;
+    }
   }
   __syncthreads();
   const int win = ds.win;
@@ -870,8 +867,8 @@ __device__ __forceinline__ int draw_chunk(const TA* __restrict__ pa, const TB* _
     const int l = tid;
     const int off = win * EPT + l;
     const bool ok = l < EPT && off < n;
-    const float a = ok ? to_f(pa[c0 + off]) : NEG_INF;
-    const float bv = (ok && TWO) ? to_f(pb[c0 + off]) : bfill;
+    const float a = ok ? ds.va[l] : NEG_INF;
+    const float bv = ok ? ds.vb[l] : bfill;
     const double w = ok ? weight(a, bv, c0 + off) : 0.0;
     double x = w;
 #pragma unroll
@@ -977,8 +974,8 @@ __device__ __forceinline__ bool has_helpers(const Params& P, const Req& R) {
 }
 
 __device__ __forceinline__ void helpers_none(const Params& P, int b) {
-  for (int c = threadIdx.x; c < P.nc; c += WG)
-    put_w(P.dec + ((int64_t)b * P.nc + c) * 2, F_NONE, 0u);
+  for (int e = threadIdx.x; e < P.nc * DEC_W; e += WG)
+    put_w(P.dec + (int64_t)b * P.nc * DEC_W + e, F_NONE, 0u);
 }
 
 // ---------------------------------------------------------------------------
@@ -1196,25 +1193,24 @@ __device__ __forceinline__ void finalize(const Params& P, int b, int cu0, int k,
     if (tid == 0) P.out[row] = t;
     if (has_helpers(P, R)) helpers_none(P, b);
   } else if (mode == 2) {
-    if (tid == 0) {
-      u64* su = P.setup[b].w;
-      const u64 sp = (u64)__double_as_longlong(fs.S[a]);
-      const u64 sq = (u64)__double_as_longlong(fs.Sq[a]);
-      st_agent(su + 0, sp & 0xffffffffull);
-      st_agent(su + 1, sp >> 32);
-      st_agent(su + 2, sq & 0xffffffffull);
-      st_agent(su + 3, sq >> 32);
-      st_agent(su + 4, (u64)__float_as_uint(fs.M[a]));
-      st_agent(su + 5, (u64)__float_as_uint(fs.Mq[a]));
-      st_agent(su + 6, (u64)(uint32_t)a);
-    }
-    // the setup is complete before any helper can see its decision word
-    if (tid == 0) stores_complete();
-    __syncthreads();
-    for (int c = tid; c < nc; c += WG) {
-      u64* dw = P.dec + ((int64_t)b * nc + c) * 2;
-      if (logits) put_w(dw + 1, 0u, __float_as_uint(st_m[(k + 1 + a) * nc + c]));
-      put_w(dw, 0u, __float_as_uint(st_m[a * nc + c]));
+    // every word of every record carries its own tag: no ordering among them
+    const u64 sp = (u64)__double_as_longlong(fs.S[a]);
+    const u64 sq = (u64)__double_as_longlong(fs.Sq[a]);
+    for (int e = tid; e < nc * DEC_W; e += WG) {
+      const int c = e / DEC_W;
+      const int f = e - c * DEC_W;
+      uint32_t pay;
+      switch (f) {
+        case 0: pay = __float_as_uint(st_m[a * nc + c]); break;
+        case 1: pay = logits ? __float_as_uint(st_m[(k + 1 + a) * nc + c]) : 0u; break;
+        case 2: pay = (uint32_t)sp; break;
+        case 3: pay = (uint32_t)(sp >> 32); break;
+        case 4: pay = (uint32_t)sq; break;
+        case 5: pay = (uint32_t)(sq >> 32); break;
+        case 6: pay = __float_as_uint(fs.M[a]); break;
+        default: pay = __float_as_uint(fs.Mq[a]); break;
+      }
+      put_w(P.dec + (int64_t)b * nc * DEC_W + e, f == 0 ? (uint32_t)a : 0u, pay);
     }
   }
   if (tid == 0) {
@@ -1265,8 +1261,8 @@ __device__ __forceinline__ void res_ctx(const Params& P, const Req& R, const Set
 }
 
 struct HelpShared {
-  float mp, mq;
-  int none, timeout, bad;
+  u64 rec[DEC_W];
+  int timeout, bad;
 };
 
 template <typename TT, typename TD, bool AL>
@@ -1276,35 +1272,28 @@ __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, i
   const Req R = load_req(P, b);
   if (!has_helpers(P, R)) return;
   const bool logits = R.kind == SV_DRAFT_LOGITS;
-  if (threadIdx.x == 0) {
-    u64* dw = P.dec + ((int64_t)b * nc + c) * 2;
-    const u64 v = take_w(dw);
-    hs.timeout = !(hi32(v) & TAG);
-    hs.none = (hi32(v) & F_NONE) != 0;
-    hs.mp = __uint_as_float(lo32(v));
-    hs.mq = 0.f;
-    if (!hs.timeout && !hs.none && logits) {
-      const u64 vq = take_w(dw + 1);
-      if (!(hi32(vq) & TAG)) hs.timeout = 1;
-      hs.mq = __uint_as_float(lo32(vq));
+  // the decision record: one word per thread, all taken at once
+  if (threadIdx.x < DEC_W) hs.rec[threadIdx.x] = take_w(P.dec + ((int64_t)b * nc + c) * DEC_W + threadIdx.x);
+  __syncthreads();
+  const bool last = c == nc - 1;
+  {
+    bool to = false;
+#pragma unroll
+    for (int f = 0; f < DEC_W; ++f) to = to || !(hi32(hs.rec[f]) & TAG);
+    if (to) {
+      if (last) write_fault(P, b, cu0, k, SV_ROW_INTERNAL);
+      return;
     }
   }
-  __syncthreads();
-  if (hs.none) return;
-  const bool last = c == nc - 1;
-  if (hs.timeout) {
-    if (last) write_fault(P, b, cu0, k, SV_ROW_INTERNAL);
-    return;
-  }
+  if (hi32(hs.rec[0]) & F_NONE) return;
   Setup su;
-  {
-    const u64* sw = P.setup[b].w;
-    su.Sp = __longlong_as_double((long long)(ld_agent(sw + 0) | (ld_agent(sw + 1) << 32)));
-    su.Sq = __longlong_as_double((long long)(ld_agent(sw + 2) | (ld_agent(sw + 3) << 32)));
-    su.Mp = __uint_as_float((uint32_t)ld_agent(sw + 4));
-    su.Mq = __uint_as_float((uint32_t)ld_agent(sw + 5));
-    su.a = (int)(uint32_t)ld_agent(sw + 6);
-  }
+  su.Sp = __longlong_as_double((long long)((u64)lo32(hs.rec[2]) | ((u64)lo32(hs.rec[3]) << 32)));
+  su.Sq = __longlong_as_double((long long)((u64)lo32(hs.rec[4]) | ((u64)lo32(hs.rec[5]) << 32)));
+  su.Mp = __uint_as_float(lo32(hs.rec[6]));
+  su.Mq = __uint_as_float(lo32(hs.rec[7]));
+  su.a = (int)(hi32(hs.rec[0]) & 63u);
+  const float cmp = __uint_as_float(lo32(hs.rec[0]));   // this chunk's maxima
+  const float cmq = logits ? __uint_as_float(lo32(hs.rec[1])) : 0.f;
   const int a = su.a;
   if (a < 0 || a >= k) {   // cannot happen after a fresh decision; never index with it
     if (last) write_fault(P, b, cu0, k, SV_ROW_INTERNAL);
@@ -1322,7 +1311,7 @@ __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, i
   int anybad;
   {
     ResCtx X;
-    res_ctx(P, R, su, hs.mp, hs.mq, trow, drow, X);
+    res_ctx(P, R, su, cmp, cmq, trow, drow, X);
     const int c0 = c * CHUNK;
     const int n = min(CHUNK, P.vocab - c0);
     Seg<TT> sp;
@@ -1396,7 +1385,7 @@ __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, i
     const int ch = ds.chunk;
     const double tl = ds.tl;
     // the chosen chunk's maxima: from the decision payloads left in the words
-    const u64* dw = P.dec + ((int64_t)b * nc + ch) * 2;
+    const u64* dw = P.dec + ((int64_t)b * nc + ch) * DEC_W;
     const float mp = __uint_as_float(lo32(ld_agent(dw)));
     const float mq = logits ? __uint_as_float(lo32(ld_agent(dw + 1))) : 0.f;
     ResCtx X;
@@ -1544,7 +1533,7 @@ __device__ __forceinline__ ReqPos req_at(const Params& P, int pos) {
 }
 
 template <typename TT, typename TD, bool AL, int E>
-__global__ __launch_bounds__(WG) void k_verify(const Params P) {
+__global__ __launch_bounds__(WG, 4) void k_verify(const Params P) {
   __shared__ Smem sm;
   __shared__ FinShared fs;
   __shared__ DrawShared ds;
@@ -1770,7 +1759,7 @@ __global__ void k_fill_zero(uint4* p, size_t n16, unsigned char* tail, size_t nt
 // host side
 // ---------------------------------------------------------------------------
 struct Layout {
-  size_t cst, dst, rx, setup, dec, res, thr_t, thr_d, total;
+  size_t cst, dst, rx, dec, res, thr_t, thr_d, total;
 };
 
 static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1786,8 +1775,7 @@ static bool layout(int batch, int total_rows, int vocab, int max_k, Layout& L, i
   L.cst = o; o = align_up(o + R * nc * 2 * sizeof(u64));
   L.dst = o; o = align_up(o + D1 * nc * 2 * sizeof(u64));
   L.rx = o; o = align_up(o + R * 3 * sizeof(u64));
-  L.setup = o; o = align_up(o + B * sizeof(SetupWords));
-  L.dec = o; o = align_up(o + B * nc * 2 * sizeof(u64));
+  L.dec = o; o = align_up(o + B * nc * DEC_W * sizeof(u64));
   L.res = o; o = align_up(o + B * nc * sizeof(u64));
   L.thr_t = o; o = align_up(o + R * sizeof(u64));
   L.thr_d = o; o = align_up(o + D1 * sizeof(u64));
@@ -1864,7 +1852,6 @@ static void carve(Params& P, void* ws, const Layout& L) {
   P.cst = (u64*)(w + L.cst);
   P.dst = (u64*)(w + L.dst);
   P.rx = (u64*)(w + L.rx);
-  P.setup = (SetupWords*)(w + L.setup);
   P.dec = (u64*)(w + L.dec);
   P.res = (u64*)(w + L.res);
   P.thr_t = (u64*)(w + L.thr_t);
