@@ -449,6 +449,11 @@ __device__ __forceinline__ float term(float v, float r, float c) {
   return __builtin_amdgcn_exp2f((v - r) * c);
 }
 
+// exp2(v * c - mc) with one rounding of the argument (v = -inf gives 0)
+__device__ __forceinline__ float fterm(float v, float c, float mc) {
+  return __builtin_amdgcn_exp2f(__builtin_fmaf(v, c, -mc));
+}
+
 // exp2((m - M) * c) in fp64 (the scale of a chunk with max m in a row with max M)
 __device__ __forceinline__ double scale_d(float m, float M, double ce) {
   return exp2(((double)m - (double)M) * ce);
@@ -611,13 +616,17 @@ __device__ __forceinline__ CStat chunk_stats(Seg<T>& sg, bool greedy, float tau,
   const float wm = wave_max(m);
   if (lane == 0) ps.m[par][w] = wm;
   // the terms against the thread's own max need no block result: they run
-  // while the other waves reach the barrier
+  // while the other waves reach the barrier.  Each term is exp2(l*c - mc) with
+  // mc = m*c rounded once and the argument rounded once (one fused
+  // multiply-add); the common factor exp2(m*c - mc) is put back exactly when the
+  // thread's sum is scaled to the chunk max below.
   float acc = 0.f, accx = 0.f;
   const bool own = m > NEG_INF && m < POS_INF;
+  const float mc = m * c;
   if (xl < 0) {
     if (own) {
 #pragma unroll
-      for (int i = 0; i < EPT; ++i) acc += term(sg.at(i), m, c);
+      for (int i = 0; i < EPT; ++i) acc += fterm(sg.at(i), c, mc);
     }
   } else {
     constexpr int VEC = VT<T>::VEC;
@@ -627,7 +636,7 @@ __device__ __forceinline__ CStat chunk_stats(Seg<T>& sg, bool greedy, float tau,
     if (own) {
 #pragma unroll
       for (int i = 0; i < EPT; ++i) {
-        const float e = term(sg.at(i), m, c);
+        const float e = fterm(sg.at(i), c, mc);
         acc += e;
         accx += (i == ix) ? 0.f : e;
       }
@@ -639,7 +648,7 @@ __device__ __forceinline__ CStat chunk_stats(Seg<T>& sg, bool greedy, float tau,
   for (int q = 1; q < NWAVE; ++q) M = fmax3nan(M, ps.m[par][q]);
   st.m = M;
   if (!(M > NEG_INF && M < POS_INF)) return st;   // empty chunk or a data fault
-  const double f = own ? (double)term(m, M, c) : 0.0;
+  const double f = own ? (double)fterm(-M, c, -mc) : 0.0;   // exp2(mc - M*c)
   const double ws = wave_sum((double)acc * f);
   double wsx = 0.0;
   if (xl >= 0) wsx = wave_sum((double)accx * f);
