@@ -81,6 +81,9 @@ constexpr uint32_t F_BAD = 0x20000000u;   // residual chunk saw an invalid proba
 // position a in the flag bits), 1 the draft chunk max, 2-3 and 4-5 the fp64
 // target and draft normalizers, 6-7 the target and draft row maxima.
 constexpr int DEC_W = 8;
+// Up to this many chunks per row, the helpers of a request exchange their
+// residual masses (nc * nc words per request); beyond, the last one gathers.
+constexpr int PEER_MAX = 32;
 
 typedef unsigned long long u64;
 
@@ -112,7 +115,7 @@ struct Params {
   u64* dst;       // [draft rows][nc][2]
   u64* rx;        // [rows][3]      values at the draft id: l_x, e_x, draft l_x or q(x)
   u64* dec;       // [batch][nc][DEC_W] helper decision records
-  u64* res;       // [batch][nc]    residual mass per chunk
+  u64* res;       // [batch][nc][nc] residual masses sent between helpers ([batch][nc] for nc > PEER_MAX)
   u64* thr_t;     // NULL when no request filters; float bits in the low half
   u64* thr_d;
   int64_t ld_t, ld_d;
@@ -837,17 +840,12 @@ struct DrawShared {
 // target is searched.  Returns the first element whose running sum exceeds tl
 // (the last positive element when rounding leaves none).
 template <typename TA, typename TB, bool TWO, typename WF>
-__device__ __forceinline__ int draw_chunk(const TA* __restrict__ pa, const TB* __restrict__ pb, bool avec,
-                          bool bvec, float bfill, int c0, int n, double tl, WF weight, Smem& sm,
-                          DrawShared& ds) {
+__device__ __forceinline__ int draw_held(const Seg<TA>& sa, const Seg<TB>& sb, float bfill, int c0,
+                                         int n, double tl, WF weight, Smem& sm, DrawShared& ds) {
   const int tid = threadIdx.x;
   const int seg = tid * EPT;               // offset of this thread's segment in the chunk
   double own = 0.0;
   int last_pos = -1;
-  Seg<TA> sa;
-  Seg<TB> sb;
-  load_contig<TA>(pa + c0, n, avec, NEG_INF, sa);
-  if (TWO) load_contig<TB>(pb + c0, n, bvec, bfill, sb);
 #pragma unroll
   for (int i = 0; i < EPT; ++i) {
     const double w = weight(sa.at(i), TWO ? sb.at(i) : 0.f, c0 + seg + i);
@@ -890,6 +888,18 @@ __device__ __forceinline__ int draw_chunk(const TA* __restrict__ pa, const TB* _
   }
   __syncthreads();
   return ds.tok;
+}
+
+// The same, loading the chunk (contiguous layout) first.
+template <typename TA, typename TB, bool TWO, typename WF>
+__device__ __forceinline__ int draw_chunk(const TA* __restrict__ pa, const TB* __restrict__ pb, bool avec,
+                          bool bvec, float bfill, int c0, int n, double tl, WF weight, Smem& sm,
+                          DrawShared& ds) {
+  Seg<TA> sa;
+  Seg<TB> sb;
+  load_contig<TA>(pa + c0, n, avec, NEG_INF, sa);
+  if (TWO) load_contig<TB>(pb + c0, n, bvec, bfill, sb);
+  return draw_held<TA, TB, TWO>(sa, sb, bfill, c0, n, tl, weight, sm, ds);
 }
 
 // Pick the chunk holding target = u*W given chunk masses in ds.E[0..nc).
@@ -1318,15 +1328,15 @@ __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, i
   const float qfill = probs ? 0.f : NEG_INF;
   double W;
   int anybad;
+  ResCtx X;
+  res_ctx(P, R, su, cmp, cmq, trow, drow, X);
+  const int c0 = c * CHUNK;
+  const int n = min(CHUNK, P.vocab - c0);
+  Seg<TT> sp;
+  Seg<TD> sq;
+  load_contig<TT>(tp + c0, n, tvec, NEG_INF, sp);
+  load_contig<TD>(dp + c0, n, dvec, qfill, sq);
   {
-    ResCtx X;
-    res_ctx(P, R, su, cmp, cmq, trow, drow, X);
-    const int c0 = c * CHUNK;
-    const int n = min(CHUNK, P.vocab - c0);
-    Seg<TT> sp;
-    Seg<TD> sq;
-    load_contig<TT>(tp + c0, n, tvec, NEG_INF, sp);
-    load_contig<TD>(dp + c0, n, dvec, qfill, sq);
     bool bad = false;
     double acc = 0.0;
     if (logits) {
@@ -1346,6 +1356,73 @@ __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, i
     }
     W = block_sum_d(acc, sm);
     anybad = block_max_i(bad ? 1 : 0, sm);
+  }
+  const double u = (double)P.u[cu0 + k];
+  if (nc <= PEER_MAX) {
+    // every helper sends its chunk's mass to every other helper of the request
+    // and takes theirs, so each picks the chunk itself; the one holding the
+    // chosen chunk draws from the registers it already has.  A helper waits here
+    // for helpers launched after it: a request's helpers are launched together,
+    // at most one request's set is partly resident at a time, and everything
+    // else finishes without waiting for helpers, so that set is completed.
+    u64* row = P.res + (int64_t)b * nc * nc;
+    const uint32_t fl = anybad ? F_BAD : 0u;
+    const uint32_t wv = __float_as_uint((float)W);
+    for (int t = threadIdx.x; t < nc; t += WG)
+      if (t != c) put_w(row + (int64_t)t * nc + c, fl, wv);
+    if (threadIdx.x == 0) {
+      hs.bad = anybad;
+      hs.timeout = 0;
+    }
+    __syncthreads();
+    int to = 0, bd = 0;
+    for (int t = threadIdx.x; t < nc; t += WG) {
+      if (t == c) {
+        ds.E[t] = (double)(float)W;
+        continue;
+      }
+      const u64 v = take_w(row + (int64_t)c * nc + t);
+      if (!(hi32(v) & TAG)) to = 1;
+      if (hi32(v) & F_BAD) bd = 1;
+      ds.E[t] = (double)__uint_as_float(lo32(v));
+    }
+    if (to) atomicOr(&hs.timeout, 1);
+    if (bd) atomicOr(&hs.bad, 1);
+    __syncthreads();
+    if (hs.timeout || hs.bad) {
+      if (last) write_fault(P, b, cu0, k, hs.timeout ? SV_ROW_INTERNAL : SV_ROW_NONFINITE);
+      return;
+    }
+    if (!pick_chunk(nc, u, ds)) {
+      if (last) {
+        const float tau = (P.thr_t && R.filt) ? thr_of(P.thr_t, trow) : NEG_INF;
+        const u64* cw = P.cst + (int64_t)trow * nc * 2;
+        const float Mp = su.Mp;
+        const double ce = R.ce;
+        auto cm = [=](int cc) { return __uint_as_float(lo32(ld_agent(cw + 2 * cc))); };
+        auto rc = [=](int cc) { return scale_d(cm(cc), Mp, ce); };
+        auto mass = [=](int cc, bool) {
+          const float m = cm(cc);
+          if (!(m > NEG_INF)) return 0.0;
+          return (double)__uint_as_float(lo32(ld_agent(cw + 2 * cc + 1))) * scale_d(m, Mp, ce);
+        };
+        const int t = draw_target_row<TT, AL>(P, R, trow, -1, tau, u, cm, mass, rc, sm, ds);
+        if (threadIdx.x == 0) P.out[trow] = t;
+      }
+      return;
+    }
+    if (ds.chunk != c) return;
+    const double tl = ds.tl;
+    int t;
+    if (logits) {
+      auto wf = [=](float lp, float lq, int) -> double { return resid_elem<true>(lp, lq, R, X); };
+      t = draw_held<TT, TD, true>(sp, sq, qfill, c0, n, tl, wf, sm, ds);
+    } else {
+      auto wf = [=](float lp, float lq, int) -> double { return resid_elem<false>(lp, lq, R, X); };
+      t = draw_held<TT, TD, true>(sp, sq, qfill, c0, n, tl, wf, sm, ds);
+    }
+    if (threadIdx.x == 0) P.out[trow] = t;
+    return;
   }
   if (!last) {
     if (threadIdx.x == 0)
@@ -1369,7 +1446,6 @@ __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, i
   if (to) atomicOr(&hs.timeout, 1);
   if (bd) atomicOr(&hs.bad, 1);
   __syncthreads();
-  const double u = (double)P.u[cu0 + k];
   if (hs.timeout) {
     write_fault(P, b, cu0, k, SV_ROW_INTERNAL);
   } else if (hs.bad) {
@@ -1397,17 +1473,17 @@ __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, i
     const u64* dw = P.dec + ((int64_t)b * nc + ch) * DEC_W;
     const float mp = __uint_as_float(lo32(ld_agent(dw)));
     const float mq = logits ? __uint_as_float(lo32(ld_agent(dw + 1))) : 0.f;
-    ResCtx X;
-    res_ctx(P, R, su, mp, mq, trow, drow, X);
-    const int c0 = ch * CHUNK;
-    const int n = min(CHUNK, P.vocab - c0);
+    ResCtx Xc;
+    res_ctx(P, R, su, mp, mq, trow, drow, Xc);
+    const int cc0 = ch * CHUNK;
+    const int cn = min(CHUNK, P.vocab - cc0);
     int t;
     if (logits) {
-      auto wf = [=](float lp, float lq, int) -> double { return resid_elem<true>(lp, lq, R, X); };
-      t = draw_chunk<TT, TD, true>(tp, dp, tvec, dvec, qfill, c0, n, tl, wf, sm, ds);
+      auto wf = [=](float lp, float lq, int) -> double { return resid_elem<true>(lp, lq, R, Xc); };
+      t = draw_chunk<TT, TD, true>(tp, dp, tvec, dvec, qfill, cc0, cn, tl, wf, sm, ds);
     } else {
-      auto wf = [=](float lp, float lq, int) -> double { return resid_elem<false>(lp, lq, R, X); };
-      t = draw_chunk<TT, TD, true>(tp, dp, tvec, dvec, qfill, c0, n, tl, wf, sm, ds);
+      auto wf = [=](float lp, float lq, int) -> double { return resid_elem<false>(lp, lq, R, Xc); };
+      t = draw_chunk<TT, TD, true>(tp, dp, tvec, dvec, qfill, cc0, cn, tl, wf, sm, ds);
     }
     if (threadIdx.x == 0) P.out[trow] = t;
   }
@@ -1785,7 +1861,7 @@ static bool layout(int batch, int total_rows, int vocab, int max_k, Layout& L, i
   L.dst = o; o = align_up(o + D1 * nc * 2 * sizeof(u64));
   L.rx = o; o = align_up(o + R * 3 * sizeof(u64));
   L.dec = o; o = align_up(o + B * nc * DEC_W * sizeof(u64));
-  L.res = o; o = align_up(o + B * nc * sizeof(u64));
+  L.res = o; o = align_up(o + B * nc * (nc <= PEER_MAX ? nc : 1) * sizeof(u64));
   L.thr_t = o; o = align_up(o + R * sizeof(u64));
   L.thr_d = o; o = align_up(o + D1 * sizeof(u64));
   L.total = o;

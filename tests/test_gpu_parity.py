@@ -322,3 +322,15 @@ def test_offsets_going_back():
     gpu, counts = check(w)
     assert counts["status"] >= 2
     assert int(gpu["status"][2]) == oracle.ROW_BAD_K and int(gpu["status"][3]) == oracle.ROW_BAD_K
+
+
+def test_residual_paths_around_the_peer_limit():
+    """Rows of 32 chunks (the helpers of a rejection exchange their residual
+    masses and the chunk's holder draws) and of 33 chunks (one helper gathers
+    the masses and re-reads the chosen chunk): draft-logit and probability
+    drafts, each path against the oracle."""
+    for V in (32 * 8192, 32 * 8192 + 1):
+        _, c2 = check(synth.make(2, seed=5, batch=8, vocab=V))
+        _, c4 = check(synth.make(4, seed=5, batch=6, vocab=V))
+        assert c2["match"] + c2["excused_accept"] + c2["excused_final"] >= 4
+        assert c4["match"] + c4["excused_accept"] + c4["excused_final"] + c4["excused_near_tie"] == 6
