@@ -17,10 +17,12 @@
 //               needs only the target row (bonus draw, one-hot draft
 //               rejection); greedy requests end here.
 //   helpers     nc workgroups per logit/probability-draft request, launched
-//               right after the next request's producers: when the finalizer
-//               reports a rejection they compute the residual mass
-//               max(0, p - q) of one chunk each; the last one picks the chunk
-//               that holds u * W, re-reads it and draws the token.
+//               some periods after the request's producers: when the
+//               finalizer reports a rejection they compute the residual mass
+//               max(0, p - q) of one chunk each and exchange the masses; the
+//               helper whose chunk holds u * W draws the token from the
+//               registers it holds (for rows of more than 32 chunks the last
+//               helper gathers the masses, re-reads the chosen chunk and draws).
 // k_thresh (only when top-k / top-p arrays are given) runs first and computes
 // each filtered row's raw-logit threshold tau (kept iff l >= tau).
 //
@@ -28,8 +30,10 @@
 // travels in a 64-bit word whose top bit is a "fresh" tag: the writer stores
 // the word with one agent-scope atomic store (coherent across the eight XCD
 // L2 caches, no fence, no counter), the single reader of that word waits for
-// the tag, takes the payload and stores the word back without its tag.  Every
-// wait is on a workgroup with a smaller launch index, and every wait is
+// the tag, takes the payload and stores the word back without its tag.
+// Producers wait for nothing; finalizers wait for producers launched before
+// them; helpers wait for their finalizer and for the other helpers of the
+// same request, which are launched together (see helper()).  Every wait is
 // bounded (a request whose wait runs out reports SV_ROW_INTERNAL).  A
 // workspace is therefore left with no tag set when a call ends.
 //
