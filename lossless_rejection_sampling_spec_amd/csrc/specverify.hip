@@ -764,18 +764,20 @@ __device__ __forceinline__ void produce(const Params& P, const Req& R, int b, in
   }
 
   if (!has_d) {
-    // target chunks only: every chunk of the strip is requested at once (the
-    // strip's bytes are in flight together), then reduced in order; past the
-    // row's last chunk the loads repeat it (never reduced)
+    // target chunks only, two in flight: chunk t+1 is requested before chunk t
+    // is reduced.  Past the row's last chunk the loads repeat it (never
+    // reduced).  Two chunks per workgroup keep the memory busy with every slot
+    // of the GPU filled, and fewer bytes queued ahead of every load shorten the
+    // dependent round trips that follow the statistics.
     constexpr int S = Strip<TT>::S;
     Buf<TT, TD> Q[S];
     Q[0] = A;
 #pragma unroll
-    for (int t = 1; t < S; ++t)
-      issue_task<TT, TD, AL>(trow, drow, false, c_begin + min(t, nt - 1), P.vocab, Q[t]);
-#pragma unroll
-    for (int t = 0; t < S; ++t)
+    for (int t = 0; t < S; ++t) {
+      if (t + 1 < S)
+        issue_task<TT, TD, AL>(trow, drow, false, c_begin + min(t + 1, nt - 1), P.vocab, Q[t + 1]);
       if (t < nt) produce_task<TT, TT, TD, AL>(P, R, Q[t], false, c_begin + t, x, tau, t, ps);
+    }
   } else {
   Buf<TT, TD> B;   // A holds the first task's loads (issued by the caller)
   int t = 0;
@@ -1521,6 +1523,7 @@ __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, i
 // not below any earlier one (the rows of valid requests never overlap).
 struct ReqPos {
   int b, cu0, cu1;
+  int cls;        // launch class: 0 sampled with draft rows, 1 other sampled, 2 greedy
   bool valid;
 };
 
@@ -1617,6 +1620,7 @@ __device__ __forceinline__ ReqPos req_at(const Params& P, int pos) {
   R.cu0 = __builtin_amdgcn_readlane(c_lo, src);
   R.cu1 = __builtin_amdgcn_readlane(c_hi, src);
   const int ra = __builtin_amdgcn_readlane(run_at, src);
+  R.cls = tc;
   R.valid = R.cu0 >= ra && req_valid(P, R.b, R.cu0, R.cu1, R.cu1 - R.cu0 - 1);
   return R;
 }
@@ -1653,7 +1657,8 @@ __global__ __launch_bounds__(WG, 4) void k_verify(const Params P) {
   }
   if (hpos >= 0) {   // helper of the request at position hpos, chunk loc - Pw
     const ReqPos Q = req_at<E>(P, hpos);
-    if (Q.valid) helper<TT, TD, AL>(P, Q.b, Q.cu0, Q.cu1 - Q.cu0 - 1, loc - Pw, sm, ds, hs);
+    // only requests with draft rows (class 0) have helper work
+    if (Q.valid && Q.cls == 0) helper<TT, TD, AL>(P, Q.b, Q.cu0, Q.cu1 - Q.cu0 - 1, loc - Pw, sm, ds, hs);
     return;
   }
   const int j = loc / P.ns;
