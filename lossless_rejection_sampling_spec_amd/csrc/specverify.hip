@@ -165,6 +165,16 @@ template <> __device__ __forceinline__ float Seg<uint16_t>::at(int i) const {
   return __uint_as_float((i & 1) ? (u & 0xffff0000u) : (u << 16));
 }
 
+// Element i (0 <= i < EPT, any lane-dependent value) of a thread's words kept in
+// LDS, in the layout of Seg::at.
+template <typename T> __device__ __forceinline__ float elem_at(const uint4* q, int i);
+template <> __device__ __forceinline__ float elem_at<float>(const uint4* q, int i) {
+  return __uint_as_float(reinterpret_cast<const uint32_t*>(q)[i]);
+}
+template <> __device__ __forceinline__ float elem_at<uint16_t>(const uint4* q, int i) {
+  return to_f(reinterpret_cast<const uint16_t*>(q)[i]);
+}
+
 // 32-bit pattern of `fill` in the element type (bf16: the upper half of f32)
 template <typename T> __device__ __forceinline__ uint32_t fill_bits(float f);
 template <> __device__ __forceinline__ uint32_t fill_bits<float>(float f) { return __float_as_uint(f); }
@@ -395,6 +405,17 @@ __device__ __forceinline__ void block_scan_d(double own, double& excl, double& i
   const double prev = __shfl_up(x, 1, 64);
   incl = x;
   excl = (lane == 0) ? carry : prev;
+}
+
+// The same scan, also returning the block total (the inclusive value of the
+// last thread, summed in the same order).
+__device__ __forceinline__ void block_scan_total_d(double own, double& excl, double& incl,
+                                                   double& total, Smem& sm) {
+  block_scan_d(own, excl, incl, sm);
+  double t = sm.d[0];
+#pragma unroll
+  for (int k = 1; k < NWAVE; ++k) t += sm.d[k];
+  total = t;
 }
 
 // A read-only input at an address that is the same in every lane, loaded
@@ -829,59 +850,52 @@ __device__ __forceinline__ void produce(const Params& P, const Req& R, int b, in
 // ---------------------------------------------------------------------------
 struct DrawShared {
   double E[MAX_NC];
-  float va[EPT], vb[EPT];   // the winning thread's elements (rows A and B)
+  uint4 qa[Seg<float>::NV], qb[Seg<float>::NV];   // the winning thread's words (rows A and B)
   double tl;
   double wexcl;
   int chunk;
   int tok;
   int win;
-  int wlast;
 };
 
-// Inverse CDF inside one chunk [c0, c0+n) of a row, in token order.  Thread
-// tid owns the segment [c0 + tid*EPT, c0 + tid*EPT + EPT).  weight(a, b, e)
-// gives the fp64 weight of element e from its values a (row A) and b (row B,
-// only when TWO); it is evaluated again, on the same inputs (handed to wave 0
-// through LDS by the thread that holds them), when the segment that holds the
-// target is searched.  Returns the first element whose running sum exceeds tl
-// (the last positive element when rounding leaves none).
+// Inverse CDF inside one chunk [c0, c0+n) of a row, in token order, once the
+// block scan of the segment sums is known.  Thread tid owns the segment
+// [c0 + tid*EPT, c0 + tid*EPT + EPT) of weight sum own, scanned into
+// [excl, incl).  weight(a, b, e) gives the fp64 weight of element e from its
+// values a (row A) and b (row B, only when TWO); it is evaluated again, on the
+// same inputs, for the one segment that is searched: its words reach wave 0
+// through LDS.  Returns the first element whose running sum exceeds tl; when
+// rounding leaves no segment holding tl (tl at or past the total), the last
+// element of positive weight.
 template <typename TA, typename TB, bool TWO, typename WF>
-__device__ __forceinline__ int draw_held(const Seg<TA>& sa, const Seg<TB>& sb, float bfill, int c0,
-                                         int n, double tl, WF weight, Smem& sm, DrawShared& ds) {
+__device__ __forceinline__ int draw_scanned(const Seg<TA>& sa, const Seg<TB>& sb, float bfill,
+                                            int c0, int n, double tl, WF weight, double own,
+                                            double excl, double incl, Smem& sm, DrawShared& ds) {
   const int tid = threadIdx.x;
-  const int seg = tid * EPT;               // offset of this thread's segment in the chunk
-  double own = 0.0;
-  int last_pos = -1;
-#pragma unroll
-  for (int i = 0; i < EPT; ++i) {
-    const double w = weight(sa.at(i), TWO ? sb.at(i) : 0.f, c0 + seg + i);
-    own += w;
-    last_pos = (w > 0.0) ? c0 + seg + i : last_pos;
-    if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound live fp64 temporaries
-  }
-  double excl, incl;
-  block_scan_d(own, excl, incl, sm);
   if (tid == 0) ds.win = -1;
   __syncthreads();
-  if (excl <= tl && tl < incl) {     // at most one thread: the intervals are disjoint
-    ds.win = tid;
+  if (excl <= tl && tl < incl) ds.win = tid;   // at most one thread: the intervals are disjoint
+  __syncthreads();
+  int win = ds.win;
+  const bool fallback = win < 0;
+  if (fallback) win = block_max_i(own > 0.0 ? tid : -1, sm);
+  if (win < 0) return -1;   // no positive weight: never drawn from
+  if (tid == win) {
     ds.wexcl = excl;
-    ds.wlast = last_pos;
 #pragma unroll
-    for (int i = 0; i < EPT; ++i) {
-      ds.va[i] = sa.at(i);
-      ds.vb[i] = TWO ? sb.at(i) : bfill;
+    for (int i = 0; i < Seg<TA>::NV; ++i) ds.qa[i] = sa.q[i];
+    if (TWO) {
+#pragma unroll
+      for (int i = 0; i < Seg<TB>::NV; ++i) ds.qb[i] = sb.q[i];
     }
   }
   __syncthreads();
-  const int win = ds.win;
-  if (win < 0) return block_max_i(last_pos, sm);   // tl at or past the chunk total
   if (tid < 64) {
     const int l = tid;
     const int off = win * EPT + l;
     const bool ok = l < EPT && off < n;
-    const float a = ok ? ds.va[l] : NEG_INF;
-    const float bv = ok ? ds.vb[l] : bfill;
+    const float a = ok ? elem_at<TA>(ds.qa, l) : NEG_INF;
+    const float bv = (ok && TWO) ? elem_at<TB>(ds.qb, l) : bfill;
     const double w = ok ? weight(a, bv, c0 + off) : 0.0;
     double x = w;
 #pragma unroll
@@ -889,11 +903,39 @@ __device__ __forceinline__ int draw_held(const Seg<TA>& sa, const Seg<TB>& sb, f
       const double y = __shfl_up(x, o, 64);
       if (l >= o) x += y;
     }
-    const uint64_t hit = __ballot(w > 0.0 && ds.wexcl + x > tl);
-    if (l == 0) ds.tok = hit ? c0 + win * EPT + (int)__builtin_ctzll(hit) : ds.wlast;
+    const uint64_t hit = fallback ? 0ull : __ballot(w > 0.0 && ds.wexcl + x > tl);
+    // no hit: the segment's last element of positive weight
+    const uint64_t pos = __ballot(w > 0.0);
+    const int lastw = pos ? c0 + win * EPT + 63 - (int)__builtin_clzll(pos) : -1;
+    if (l == 0) ds.tok = hit ? c0 + win * EPT + (int)__builtin_ctzll(hit) : lastw;
   }
   __syncthreads();
   return ds.tok;
+}
+
+// Weight sum of this thread's segment, in element order (the order the draw's
+// scan assumes).
+template <typename TA, typename TB, bool TWO, typename WF>
+__device__ __forceinline__ double seg_weights(const Seg<TA>& sa, const Seg<TB>& sb, int c0,
+                                              WF weight) {
+  const int seg = threadIdx.x * EPT;
+  double own = 0.0;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    own += weight(sa.at(i), TWO ? sb.at(i) : 0.f, c0 + seg + i);
+    if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound live fp64 temporaries
+  }
+  return own;
+}
+
+// The draw over a chunk whose segment sums are not known yet.
+template <typename TA, typename TB, bool TWO, typename WF>
+__device__ __forceinline__ int draw_held(const Seg<TA>& sa, const Seg<TB>& sb, float bfill, int c0,
+                                         int n, double tl, WF weight, Smem& sm, DrawShared& ds) {
+  const double own = seg_weights<TA, TB, TWO>(sa, sb, c0, weight);
+  double excl, incl;
+  block_scan_d(own, excl, incl, sm);
+  return draw_scanned<TA, TB, TWO>(sa, sb, bfill, c0, n, tl, weight, own, excl, incl, sm, ds);
 }
 
 // The same, loading the chunk (contiguous layout) first.
@@ -1248,6 +1290,7 @@ __device__ __forceinline__ void finalize(const Params& P, int b, int cu0, int k,
 // helpers: residual max(0, p - q) at the first rejection
 // ---------------------------------------------------------------------------
 struct ResCtx {
+  float c;         // log2(e) / T of the request
   float mp, mq;    // chunk maxima of target and draft
   double sp, sq;   // per-chunk scale R_c / S of target and draft
   float taup, tauq;
@@ -1256,13 +1299,13 @@ struct ResCtx {
 // Residual weight of one token from its target value lp and draft value lq
 // (logit, or probability for a probability draft).
 template <bool LOGITS>
-__device__ __forceinline__ double resid_elem(float lp, float lq, const Req& R, const ResCtx& X) {
+__device__ __forceinline__ double resid_elem(float lp, float lq, const ResCtx& X) {
   if (lp < X.taup) lp = NEG_INF;
-  const double p = (double)term(lp, X.mp, R.c) * X.sp;
+  const double p = (double)term(lp, X.mp, X.c) * X.sp;
   double q;
   if (LOGITS) {
     if (lq < X.tauq) lq = NEG_INF;
-    q = (double)term(lq, X.mq, R.c) * X.sq;
+    q = (double)term(lq, X.mq, X.c) * X.sq;
   } else {
     q = (double)lq;
   }
@@ -1272,6 +1315,7 @@ __device__ __forceinline__ double resid_elem(float lp, float lq, const Req& R, c
 
 __device__ __forceinline__ void res_ctx(const Params& P, const Req& R, const Setup& su, float mp,
                                         float mq, int trow, int drow, ResCtx& X) {
+  X.c = R.c;
   X.mp = (mp > NEG_INF) ? mp : 0.f;
   X.sp = (mp > NEG_INF) ? scale_d(mp, su.Mp, R.ce) / su.Sp : 0.0;
   X.taup = (P.thr_t && R.filt) ? thr_of(P.thr_t, trow) : NEG_INF;
@@ -1342,25 +1386,26 @@ __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, i
   Seg<TD> sq;
   load_contig<TT>(tp + c0, n, tvec, NEG_INF, sp);
   load_contig<TD>(dp + c0, n, dvec, qfill, sq);
+  // the chunk's residual mass as the total of a block scan of the segment
+  // sums: the scan, the segment sums and the last positive elements are kept
+  // for the draw, which then evaluates only the winning segment again
+  auto wl = [=](float lp, float lq, int) -> double { return resid_elem<true>(lp, lq, X); };
+  auto wpr = [=](float lp, float lq, int) -> double { return resid_elem<false>(lp, lq, X); };
+  double own;
   {
     bool bad = false;
-    double acc = 0.0;
     if (logits) {
-#pragma unroll
-      for (int i = 0; i < EPT; ++i) {
-        acc += resid_elem<true>(sp.at(i), sq.at(i), R, X);
-        if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound live fp64 temporaries
-      }
+      own = seg_weights<TT, TD, true>(sp, sq, c0, wl);
     } else {
+      own = seg_weights<TT, TD, true>(sp, sq, c0, wpr);
 #pragma unroll
       for (int i = 0; i < EPT; ++i) {
         const float lq = sq.at(i);
-        acc += resid_elem<false>(sp.at(i), lq, R, X);
         bad = bad || !(lq >= 0.f && lq < POS_INF);
-        if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
       }
     }
-    W = block_sum_d(acc, sm);
+    double excl, incl;
+    block_scan_total_d(own, excl, incl, W, sm);
     anybad = block_max_i(bad ? 1 : 0, sm);
   }
   const double u = (double)P.u[cu0 + k];
@@ -1420,13 +1465,12 @@ __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, i
     if (ds.chunk != c) return;
     const double tl = ds.tl;
     int t;
-    if (logits) {
-      auto wf = [=](float lp, float lq, int) -> double { return resid_elem<true>(lp, lq, R, X); };
-      t = draw_held<TT, TD, true>(sp, sq, qfill, c0, n, tl, wf, sm, ds);
-    } else {
-      auto wf = [=](float lp, float lq, int) -> double { return resid_elem<false>(lp, lq, R, X); };
-      t = draw_held<TT, TD, true>(sp, sq, qfill, c0, n, tl, wf, sm, ds);
-    }
+    double excl, incl;
+    block_scan_d(own, excl, incl, sm);
+    if (logits)
+      t = draw_scanned<TT, TD, true>(sp, sq, qfill, c0, n, tl, wl, own, excl, incl, sm, ds);
+    else
+      t = draw_scanned<TT, TD, true>(sp, sq, qfill, c0, n, tl, wpr, own, excl, incl, sm, ds);
     if (threadIdx.x == 0) P.out[trow] = t;
     return;
   }
@@ -1485,10 +1529,10 @@ __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, i
     const int cn = min(CHUNK, P.vocab - cc0);
     int t;
     if (logits) {
-      auto wf = [=](float lp, float lq, int) -> double { return resid_elem<true>(lp, lq, R, Xc); };
+      auto wf = [=](float lp, float lq, int) -> double { return resid_elem<true>(lp, lq, Xc); };
       t = draw_chunk<TT, TD, true>(tp, dp, tvec, dvec, qfill, cc0, cn, tl, wf, sm, ds);
     } else {
-      auto wf = [=](float lp, float lq, int) -> double { return resid_elem<false>(lp, lq, R, Xc); };
+      auto wf = [=](float lp, float lq, int) -> double { return resid_elem<false>(lp, lq, Xc); };
       t = draw_chunk<TT, TD, true>(tp, dp, tvec, dvec, qfill, cc0, cn, tl, wf, sm, ds);
     }
     if (threadIdx.x == 0) P.out[trow] = t;
