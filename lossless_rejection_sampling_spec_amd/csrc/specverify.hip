@@ -17,7 +17,7 @@
 //               needs only the target row (bonus draw, one-hot draft
 //               rejection); greedy requests end here.
 //   helpers     nc workgroups per logit/probability-draft request, launched
-//               some periods after the request's producers: when the
+//               after every producer of the call: when the
 //               finalizer reports a rejection they compute the residual mass
 //               max(0, p - q) of one chunk each and exchange the masses; the
 //               helper whose chunk holds u * W draws the token from the
@@ -67,12 +67,6 @@ constexpr int CHUNK = 8192;
 constexpr int EPT = CHUNK / WG;   // elements per thread per chunk
 constexpr int MAX_NC = 512;       // chunks per row (vocab <= 4,194,304)
 constexpr int MAX_K = 63;         // k+1 positions fit one wave
-// Bytes streamed between a request's producers and its helpers (about the time
-// its finalizer needs to decide).
-#ifndef SV_HELPER_DELAY_MB
-#define SV_HELPER_DELAY_MB 64
-#endif
-constexpr double HELPER_DELAY_BYTES = SV_HELPER_DELAY_MB * 1048576.0;
 constexpr int STAGE_MAX = 49152;  // bytes of LDS the finalizer may stage statistics in
 constexpr int SPIN_MAX = 1 << 18; // polls before a wait gives up
 constexpr float NEG_INF = -__builtin_inff();
@@ -127,7 +121,6 @@ struct Params {
   int S;          // chunks per producer strip
   int ns;         // strips per row
   int H;          // helper workgroups per request (nc, or 0 for the greedy entry)
-  int dwg;        // periods between a request's producers and its helpers
   int greedy_entry;
 };
 
@@ -1541,14 +1534,13 @@ __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, i
 
 // ---------------------------------------------------------------------------
 // k_verify: block index -> role
-//   The launch is a sequence of periods p = 0, 1, ...: period p holds the
-//   producers of the request at launch position p ((max_k+1) * ns workgroups,
-//   row j, strip s; p < batch), then the helpers of the request at position
-//   p - D (H workgroups; 0 <= p - D < batch).  The D periods between a
-//   request's producers and its helpers give its finalizer the time to decide
-//   (the host sizes D from the bytes the periods stream), and the sampled
-//   requests with draft rows -- the only ones whose helpers have work -- come
-//   first, so their residual draws run while later requests still stream.
+//   The producers of every request come first, request by request in launch
+//   order ((max_k+1) * ns workgroups per request: row j, strip s), then the
+//   helpers, H workgroups per request in the same order.  The sampled requests
+//   with draft rows -- the only ones whose helpers have work -- are launched
+//   first, so their finalizers decide while later requests still stream, and
+//   their helpers, dispatched as the last producers start, find the decision
+//   posted or close to it instead of holding a slot through the streaming.
 // ---------------------------------------------------------------------------
 // ---------------------------------------------------------------------------
 // launch order of the requests
@@ -1678,33 +1670,18 @@ __global__ __launch_bounds__(WG, 4) void k_verify(const Params P) {
   __shared__ ProdShared ps;
   extern __shared__ uint32_t stage[];
   const int Pw = (P.max_k + 1) * P.ns;
-  const int H = P.H;
-  const int Dp = H > 0 ? min(P.dwg, P.batch) : P.batch;
   const long long id = blockIdx.x;
-  const long long seg1 = (long long)Dp * Pw;                       // periods 0 .. Dp-1
-  const long long seg2 = (long long)(P.batch - Dp) * (Pw + H);     // periods Dp .. batch-1
-  int per, loc, hpos = -1;
-  if (id < seg1) {
-    per = (int)(id / Pw);
-    loc = (int)(id - (long long)per * Pw);
-  } else if (id < seg1 + seg2) {
-    const long long rest = id - seg1;
-    const int q = (int)(rest / (Pw + H));
-    per = Dp + q;
-    loc = (int)(rest - (long long)q * (Pw + H));
-    if (loc >= Pw) hpos = per - Dp;
-  } else {                                                         // helpers of the last Dp positions
-    const long long rest = id - seg1 - seg2;
-    per = P.batch;
-    hpos = P.batch - Dp + (int)(rest / H);
-    loc = Pw + (int)(rest % H);
-  }
-  if (hpos >= 0) {   // helper of the request at position hpos, chunk loc - Pw
+  const long long np = (long long)P.batch * Pw;   // producer workgroups
+  if (id >= np) {   // helper of the request at position hpos, chunk c
+    const int hpos = (int)((id - np) / P.H);
+    const int c = (int)(id - np - (long long)hpos * P.H);
     const ReqPos Q = req_at<E>(P, hpos);
     // only requests with draft rows (class 0) have helper work
-    if (Q.valid && Q.cls == 0) helper<TT, TD, AL>(P, Q.b, Q.cu0, Q.cu1 - Q.cu0 - 1, loc - Pw, sm, ds, hs);
+    if (Q.valid && Q.cls == 0) helper<TT, TD, AL>(P, Q.b, Q.cu0, Q.cu1 - Q.cu0 - 1, c, sm, ds, hs);
     return;
   }
+  const int per = (int)(id / Pw);
+  const int loc = (int)(id - (long long)per * Pw);
   const int j = loc / P.ns;
   const int s = loc - j * P.ns;
   const ReqPos Q = req_at<E>(P, per);
@@ -1929,11 +1906,6 @@ static long long verify_grid(const Params& P) {
 template <typename TT, typename TD>
 static int launch_all(Params P, bool sampled, bool filters, bool aligned, hipStream_t st) {
   P.S = Strip<TT>::S;   // at most 8: a strip's statistics fit ProdShared::pub
-  {
-    // helper delay: the periods streaming about HELPER_DELAY_BYTES
-    const double per_bytes = (double)P.total_rows / P.batch * P.vocab * sizeof(TT);
-    P.dwg = (int)std::min<double>(P.batch, std::max(1.0, std::ceil(HELPER_DELAY_BYTES / per_bytes)));
-  }
   P.ns = (P.nc + P.S - 1) / P.S;
   P.H = sampled ? P.nc : 0;
   const long long g = verify_grid<TT>(P);
