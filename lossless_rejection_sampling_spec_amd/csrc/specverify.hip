@@ -507,6 +507,26 @@ __device__ __forceinline__ double dpp_d(double x) {
   const int hi = dpp_i<CTRL>((int)(uint32_t)(v >> 32));
   return __longlong_as_double((long long)(((u64)(uint32_t)hi << 32) | (u64)(uint32_t)lo));
 }
+// x from the lane CTRL names, +0.0 where the control names no lane (bound off)
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_or0_d(double x) {
+  const long long v = __double_as_longlong(x);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROWS, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, ROWS, 0xf, false);
+  return __longlong_as_double((long long)(((u64)(uint32_t)hi << 32) | (u64)(uint32_t)lo));
+}
+static_assert(EPT == 32, "the draw's segment scan covers 32 lanes");
+// Inclusive fp64 scan over lanes 0..31 (row shifts of 1, 2, 4, 8, then row 0's
+// last value into row 1); lanes 32..63 hold their own partial values.
+__device__ __forceinline__ double scan32_d(double x) {
+  x += dpp_or0_d<0x111, 0xf>(x);   // row_shr:1
+  x += dpp_or0_d<0x112, 0xf>(x);   // row_shr:2
+  x += dpp_or0_d<0x114, 0xf>(x);   // row_shr:4
+  x += dpp_or0_d<0x118, 0xf>(x);   // row_shr:8
+  x += dpp_or0_d<0x142, 0x2>(x);   // row_bcast:15 into row 1
+  return x;
+}
+
 constexpr int DPP_XOR1 = 0xB1;      // quad_perm [1,0,3,2]
 constexpr int DPP_XOR2 = 0x4E;      // quad_perm [2,3,0,1]
 constexpr int DPP_HMIRROR = 0x141;  // lane i <-> 7 - i within each 8
@@ -890,12 +910,7 @@ __device__ __forceinline__ int draw_scanned(const Seg<TA>& sa, const Seg<TB>& sb
     const float a = ok ? elem_at<TA>(ds.qa, l) : NEG_INF;
     const float bv = (ok && TWO) ? elem_at<TB>(ds.qb, l) : bfill;
     const double w = ok ? weight(a, bv, c0 + off) : 0.0;
-    double x = w;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const double y = __shfl_up(x, o, 64);
-      if (l >= o) x += y;
-    }
+    const double x = scan32_d(w);   // EPT = 32 elements: lanes 0..31
     const uint64_t hit = fallback ? 0ull : __ballot(w > 0.0 && ds.wexcl + x > tl);
     // no hit: the segment's last element of positive weight
     const uint64_t pos = __ballot(w > 0.0);
@@ -1384,7 +1399,7 @@ __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, i
   // for the draw, which then evaluates only the winning segment again
   auto wl = [=](float lp, float lq, int) -> double { return resid_elem<true>(lp, lq, X); };
   auto wpr = [=](float lp, float lq, int) -> double { return resid_elem<false>(lp, lq, X); };
-  double own;
+  double own, excl, incl;
   {
     bool bad = false;
     if (logits) {
@@ -1397,7 +1412,6 @@ __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, i
         bad = bad || !(lq >= 0.f && lq < POS_INF);
       }
     }
-    double excl, incl;
     block_scan_total_d(own, excl, incl, W, sm);
     anybad = block_max_i(bad ? 1 : 0, sm);
   }
@@ -1458,8 +1472,6 @@ __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, i
     if (ds.chunk != c) return;
     const double tl = ds.tl;
     int t;
-    double excl, incl;
-    block_scan_d(own, excl, incl, sm);
     if (logits)
       t = draw_scanned<TT, TD, true>(sp, sq, qfill, c0, n, tl, wl, own, excl, incl, sm, ds);
     else
