@@ -109,8 +109,9 @@ struct Params {
   float* p_at;
   float* q_at;
   int32_t* status;
-  u64* cst;       // [rows][nc][2]  target chunk max / (sum or argmax)
-  u64* dst;       // [draft rows][nc][2]
+  u64* cst;       // [rows][nc]     target chunk statistics: max in the low half, sum or
+                  //                argmax in the high half below the tag (never negative)
+  u64* dst;       // [draft rows][nc]
   u64* rx;        // [rows][3]      values at the draft id: l_x, e_x, draft l_x or q(x)
   u64* dec;       // [batch][nc][DEC_W] helper decision records
   u64* res;       // [batch][nc][nc] residual masses sent between helpers ([batch][nc] for nc > PEER_MAX)
@@ -838,9 +839,10 @@ __device__ __forceinline__ void produce(const Params& P, const Req& R, int b, in
   if (tp < nt) {
     const bool is_d = (tp & sh) != 0;
     const int c = c_begin + (tp >> sh);
-    u64* w = is_d ? P.dst + ((int64_t)(d0 + j) * nc + c) * 2 : P.cst + ((int64_t)row * nc + c) * 2;
-    put_w(w, 0u, ps.pub[tp][0]);
-    put_w(w + 1, 0u, ps.pub[tp][1]);
+    // one word per chunk: the sum (or argmax) is never negative, so its top
+    // bit is free for the tag
+    u64* w = is_d ? P.dst + ((int64_t)(d0 + j) * nc + c) : P.cst + ((int64_t)row * nc + c);
+    put_w(w, ps.pub[tp][1] & ~TAG, ps.pub[tp][0]);
     const int c0 = c * CHUNK;
     if (!is_d && x >= c0 && x < c0 + min(CHUNK, P.vocab - c0))
       put_w(P.rx + (int64_t)row * 3 + 1, 0u, ps.pub[tp][2]);
@@ -1086,8 +1088,8 @@ __device__ __forceinline__ void finalize(const Params& P, int b, int cu0, int k,
   if (!R.bad_param) {
     // wait for, stage and consume every word the request's producers published
     // (also when a draft id is out of range: the statistics were still written)
-    const int nA = (k + 1) * nc * 2;
-    const int nB = logits ? k * nc * 2 : 0;
+    const int nA = (k + 1) * nc;
+    const int nB = logits ? k * nc : 0;
     const int rxw = sampled ? ((R.kind == SV_DRAFT_ONEHOT) ? 2 : 3) : 0;
     const int nC = k * rxw;
     int to = 0;
@@ -1095,18 +1097,16 @@ __device__ __forceinline__ void finalize(const Params& P, int b, int cu0, int k,
       u64* src;
       int slot = -1, c = 0, f = 0, jr = 0;
       if (w < nA) {
-        jr = w / (2 * nc);
-        c = (w / 2) % nc;
-        f = w & 1;
+        jr = w / nc;
+        c = w - jr * nc;
         slot = jr;
-        src = P.cst + ((int64_t)(cu0 + jr) * nc + c) * 2 + f;
+        src = P.cst + ((int64_t)(cu0 + jr) * nc + c);
       } else if (w < nA + nB) {
         const int w2 = w - nA;
-        jr = w2 / (2 * nc);
-        c = (w2 / 2) % nc;
-        f = w2 & 1;
+        jr = w2 / nc;
+        c = w2 - jr * nc;
         slot = k + 1 + jr;
-        src = P.dst + ((int64_t)(d0 + jr) * nc + c) * 2 + f;
+        src = P.dst + ((int64_t)(d0 + jr) * nc + c);
       } else {
         const int w3 = w - nA - nB;
         jr = w3 / rxw;
@@ -1118,8 +1118,8 @@ __device__ __forceinline__ void finalize(const Params& P, int b, int cu0, int k,
       if (!(hi32(v) & TAG)) to = 1;
       const uint32_t pay = lo32(v);
       if (slot >= 0) {
-        if (f == 0) st_m[slot * nc + c] = __uint_as_float(pay);
-        else st_s[slot * nc + c] = pay;
+        st_m[slot * nc + c] = __uint_as_float(pay);
+        st_s[slot * nc + c] = hi32(v) & ~TAG;
       } else if (f == 0) {
         fs.lx[jr] = __uint_as_float(pay);
       } else if (f == 1) {
@@ -1454,15 +1454,15 @@ __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, i
     if (!pick_chunk(nc, u, ds)) {
       if (last) {
         const float tau = (P.thr_t && R.filt) ? thr_of(P.thr_t, trow) : NEG_INF;
-        const u64* cw = P.cst + (int64_t)trow * nc * 2;
+        const u64* cw = P.cst + (int64_t)trow * nc;
         const float Mp = su.Mp;
         const double ce = R.ce;
-        auto cm = [=](int cc) { return __uint_as_float(lo32(ld_agent(cw + 2 * cc))); };
+        auto cm = [=](int cc) { return __uint_as_float(lo32(ld_agent(cw + cc))); };
         auto rc = [=](int cc) { return scale_d(cm(cc), Mp, ce); };
         auto mass = [=](int cc, bool) {
           const float m = cm(cc);
           if (!(m > NEG_INF)) return 0.0;
-          return (double)__uint_as_float(lo32(ld_agent(cw + 2 * cc + 1))) * scale_d(m, Mp, ce);
+          return (double)__uint_as_float(hi32(ld_agent(cw + cc)) & ~TAG) * scale_d(m, Mp, ce);
         };
         const int t = draw_target_row<TT, AL>(P, R, trow, -1, tau, u, cm, mass, rc, sm, ds);
         if (threadIdx.x == 0) P.out[trow] = t;
@@ -1509,15 +1509,15 @@ __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, i
     // residual mass is exactly zero: draw from p of the rejected row, using the
     // row's chunk statistics (their payloads stay in the words after consumption)
     const float tau = (P.thr_t && R.filt) ? thr_of(P.thr_t, trow) : NEG_INF;
-    const u64* cw = P.cst + (int64_t)trow * nc * 2;
+    const u64* cw = P.cst + (int64_t)trow * nc;
     const float Mp = su.Mp;
     const double ce = R.ce;
-    auto cm = [=](int cc) { return __uint_as_float(lo32(ld_agent(cw + 2 * cc))); };
+    auto cm = [=](int cc) { return __uint_as_float(lo32(ld_agent(cw + cc))); };
     auto rc = [=](int cc) { return scale_d(cm(cc), Mp, ce); };
     auto mass = [=](int cc, bool) {
       const float m = cm(cc);
       if (!(m > NEG_INF)) return 0.0;
-      return (double)__uint_as_float(lo32(ld_agent(cw + 2 * cc + 1))) * scale_d(m, Mp, ce);
+      return (double)__uint_as_float(hi32(ld_agent(cw + cc)) & ~TAG) * scale_d(m, Mp, ce);
     };
     const int t = draw_target_row<TT, AL>(P, R, trow, -1, tau, u, cm, mass, rc, sm, ds);
     if (threadIdx.x == 0) P.out[trow] = t;
@@ -1899,8 +1899,8 @@ static bool layout(int batch, int total_rows, int vocab, int max_k, Layout& L, i
   const size_t B = (size_t)batch, R = (size_t)total_rows, D = (size_t)(total_rows - batch);
   const size_t D1 = D ? D : 1;
   size_t o = 0;
-  L.cst = o; o = align_up(o + R * nc * 2 * sizeof(u64));
-  L.dst = o; o = align_up(o + D1 * nc * 2 * sizeof(u64));
+  L.cst = o; o = align_up(o + R * nc * sizeof(u64));
+  L.dst = o; o = align_up(o + D1 * nc * sizeof(u64));
   L.rx = o; o = align_up(o + R * 3 * sizeof(u64));
   L.dec = o; o = align_up(o + B * nc * DEC_W * sizeof(u64));
   L.res = o; o = align_up(o + B * nc * (nc <= PEER_MAX ? nc : 1) * sizeof(u64));
