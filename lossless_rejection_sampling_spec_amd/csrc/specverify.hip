@@ -39,16 +39,22 @@
 //
 // Numerics (temperature T, c = log2(e)/T rounded to fp32; every fp64 step
 // uses that same c, so all terms share one temperature):
-//   element term    exp2((l - r) * c) in fp32 against a reference r >= l (a
-//                   thread's own max in the producers, the chunk max elsewhere).
+//   element term    in fp32 against a reference r >= l: in the producers
+//                   exp2(l*c - m*c) with r = m the thread's own max, m*c
+//                   rounded once and the argument formed by one fused
+//                   multiply-add; in the finalizer and the helpers
+//                   exp2((l - r) * c) with r the chunk max.
 //   chunk sum       s_c = sum over threads of (fp32 sum of the thread's terms)
 //                   * exp2((m_t - m_c) * c), rescaled and added in fp64 and
 //                   published as fp32 with the chunk max m_c.
 //   chunk merge     S = sum_c s_c * exp2((m_c - M) * c) in fp64, in chunk order.
 //   gathered p(x)   exp2((l_x - M) * c) / S in fp64; acceptance u*q(x) < p(x)
 //                   in fp64.
-//   final draw      chunk masses in fp64, sequential prefix over chunks, then a
-//                   fp64 block scan over the chosen chunk in token order.
+//   final draw      per-element weights in fp64; a chunk's mass is the total
+//                   of an fp64 block scan of its segment sums, exchanged
+//                   between helpers rounded to fp32; sequential prefix over
+//                   chunks in fp64, then the scan inside the chosen chunk in
+//                   token order.
 
 #include <hip/hip_runtime.h>
 #include <float.h>
