@@ -47,7 +47,9 @@
 //   chunk sum       s_c = sum over threads of (fp32 sum of the thread's terms)
 //                   * exp2((m_t - m_c) * c), rescaled and added in fp64 and
 //                   published as fp32 with the chunk max m_c.
-//   chunk merge     S = sum_c s_c * exp2((m_c - M) * c) in fp64, in chunk order.
+//   chunk merge     S = sum_c s_c * exp2((m_c - M) * c) in fp64: 16 lanes per
+//                   row take chunks c = lane, lane + 16, ... in order, then a
+//                   fixed butterfly adds the 16 partial sums.
 //   gathered p(x)   exp2((l_x - M) * c) / S in fp64; acceptance u*q(x) < p(x)
 //                   in fp64.
 //   final draw      per-element weights in fp64; a chunk's mass is the total
@@ -1067,6 +1069,7 @@ __device__ __forceinline__ void helpers_none(const Params& P, int b) {
 struct FinShared {
   float M[64], Mq[64];
   double S[64], Sq[64];
+  int g[64];
   float lx[64], sx[64], dlx[64];
   int x[64];
   int a, code, mode, timeout;
@@ -1138,25 +1141,60 @@ __device__ __forceinline__ void finalize(const Params& P, int b, int cu0, int k,
   }
   __syncthreads();
 
-  // row maxima (one thread per staged row: target rows 0..k, draft rows 0..k-1)
+  // staged rows (target rows 0..k, then draft rows 0..k-1), 16 lanes per row
+  // (one DPP row): the row max; for sampled rows each chunk sum scaled to the
+  // row max, in place, and the fp64 total of the scaled sums (lane-strided
+  // partial sums, then a fixed butterfly over the 16 lanes); for greedy rows
+  // the lowest chunk that holds the max
   const bool staged = !R.bad_param && !badtok_any && !fs.timeout;
   const int nrows = (k + 1) + (logits ? k : 0);
-  if (staged && tid < nrows) {
-    float Mr = NEG_INF;
-    for (int c = 0; c < nc; ++c) Mr = fmax3nan(Mr, st_m[tid * nc + c]);
-    if (tid <= k) fs.M[tid] = Mr;
-    else fs.Mq[tid - k - 1] = Mr;
-  }
-  __syncthreads();
-  // sampled rows: each chunk sum scaled to its row max, in place (all threads)
-  if (staged && sampled) {
-    for (int e = tid; e < nrows * nc; e += WG) {
-      const int slot = e / nc;
-      const float Mr = slot <= k ? fs.M[slot] : fs.Mq[slot - k - 1];
-      const float m = st_m[e];
-      float v = 0.f;
-      if (Mr > NEG_INF && Mr < POS_INF && m > NEG_INF) v = __uint_as_float(st_s[e]) * term(m, Mr, R.c);
-      st_s[e] = __float_as_uint(v);
+  if (staged) {
+    const int sub = tid & 15;
+    for (int r = tid >> 4; r < nrows; r += WG / 16) {   // the same r in all 16 lanes of a row
+      const float* mrow = st_m + r * nc;
+      uint32_t* srow = st_s + r * nc;
+      float Ml = NEG_INF;
+      for (int c = sub; c < nc; c += 16) Ml = fmax3nan(Ml, mrow[c]);
+      Ml = fmax3nan(Ml, dpp_f<DPP_XOR1>(Ml));
+      Ml = fmax3nan(Ml, dpp_f<DPP_XOR2>(Ml));
+      Ml = fmax3nan(Ml, dpp_f<DPP_HMIRROR>(Ml));
+      const float Mr = fmax3nan(Ml, dpp_f<DPP_MIRROR>(Ml));
+      if (sampled) {
+        const bool fin = Mr > NEG_INF && Mr < POS_INF;
+        double Sl = 0.0;
+        for (int c = sub; c < nc; c += 16) {
+          const float m = mrow[c];
+          float v = 0.f;
+          if (fin && m > NEG_INF) v = __uint_as_float(srow[c]) * term(m, Mr, R.c);
+          srow[c] = __float_as_uint(v);
+          Sl += (double)v;
+        }
+        Sl += dpp_d<DPP_XOR1>(Sl);
+        Sl += dpp_d<DPP_XOR2>(Sl);
+        Sl += dpp_d<DPP_HMIRROR>(Sl);
+        Sl += dpp_d<DPP_MIRROR>(Sl);
+        if (sub == 0) {
+          if (r <= k) {
+            fs.M[r] = Mr;
+            fs.S[r] = Sl;
+          } else {
+            fs.Mq[r - k - 1] = Mr;
+            fs.Sq[r - k - 1] = Sl;
+          }
+        }
+      } else {
+        int cl = INT32_MAX;
+        for (int c = sub; c < nc; c += 16)
+          if (cl == INT32_MAX && mrow[c] == Mr) cl = c;
+        cl = min(cl, dpp_i<DPP_XOR1>(cl));
+        cl = min(cl, dpp_i<DPP_XOR2>(cl));
+        cl = min(cl, dpp_i<DPP_HMIRROR>(cl));
+        cl = min(cl, dpp_i<DPP_MIRROR>(cl));
+        if (sub == 0) {
+          fs.M[r] = Mr;
+          fs.g[r] = cl < nc ? cl * CHUNK + (int)srow[cl] : -1;
+        }
+      }
     }
   }
   __syncthreads();
@@ -1168,25 +1206,14 @@ __device__ __forceinline__ void finalize(const Params& P, int b, int cu0, int k,
     double S = 0.0, Sq = 0.0;
     int g = -1;
     if (j <= k && staged) {
-      const float* mrow = st_m + j * nc;
-      const uint32_t* srow = st_s + j * nc;
       M = fs.M[j];
-      if (R.greedy) {
-        for (int c = 0; c < nc; ++c) {
-          if (mrow[c] == M) {
-            g = c * CHUNK + (int)srow[c];
-            break;
-          }
-        }
-      } else {
-        for (int c = 0; c < nc; ++c) S += (double)__uint_as_float(srow[c]);
-      }
+      if (R.greedy) g = fs.g[j];
+      else S = fs.S[j];
       nonfin = (M != M) || M == POS_INF;
       empty = M == NEG_INF;
       if (logits && j < k) {
-        const uint32_t* qs = st_s + (k + 1 + j) * nc;
         Mq = fs.Mq[j];
-        for (int c = 0; c < nc; ++c) Sq += (double)__uint_as_float(qs[c]);
+        Sq = fs.Sq[j];
         nonfin = nonfin || (Mq != Mq) || Mq == POS_INF;
         empty = empty || Mq == NEG_INF;
       }
