@@ -525,6 +525,17 @@ __device__ __forceinline__ double dpp_or0_d(double x) {
   return __longlong_as_double((long long)(((u64)(uint32_t)hi << 32) | (u64)(uint32_t)lo));
 }
 static_assert(EPT == 32, "the draw's segment scan covers 32 lanes");
+// Inclusive fp64 scan over the wave: row shifts of 1, 2, 4, 8, then the last
+// value of rows 0 and 2 into rows 1 and 3, then lane 31 into rows 2 and 3.
+__device__ __forceinline__ double scan64_d(double x) {
+  x += dpp_or0_d<0x111, 0xf>(x);   // row_shr:1
+  x += dpp_or0_d<0x112, 0xf>(x);   // row_shr:2
+  x += dpp_or0_d<0x114, 0xf>(x);   // row_shr:4
+  x += dpp_or0_d<0x118, 0xf>(x);   // row_shr:8
+  x += dpp_or0_d<0x142, 0xa>(x);   // row_bcast:15 into rows 1 and 3
+  x += dpp_or0_d<0x143, 0xc>(x);   // row_bcast:31 into rows 2 and 3
+  return x;
+}
 // Inclusive fp64 scan over lanes 0..31 (row shifts of 1, 2, 4, 8, then row 0's
 // last value into row 1); lanes 32..63 hold their own partial values.
 __device__ __forceinline__ double scan32_d(double x) {
@@ -969,35 +980,49 @@ __device__ __forceinline__ int draw_chunk(const TA* __restrict__ pa, const TB* _
 }
 
 // Pick the chunk holding target = u*W given chunk masses in ds.E[0..nc).
-// Returns false when W == 0.  Thread 0 computes; result in ds.chunk, ds.tl.
+// Returns false when W == 0.  Wave 0 scans the masses in blocks of 64 chunks
+// (an fp64 wave scan per block, blocks added in order; W is the last prefix,
+// so the prefixes and W round alike); result in ds.chunk and ds.tl (target
+// minus the prefix before the chunk; +inf when rounding leaves no chunk past
+// the target, which then picks the last chunk of positive mass).
 __device__ __forceinline__ bool pick_chunk(int nc, double u, DrawShared& ds) {
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (threadIdx.x < 64) {
+    const int l = threadIdx.x;
     double W = 0.0;
-    for (int c = 0; c < nc; ++c) W += ds.E[c];
+    for (int c0 = 0; c0 < nc; c0 += 64) {
+      const double e = (c0 + l < nc) ? ds.E[c0 + l] : 0.0;
+      W += rl_d(scan64_d(e), 63);
+    }
     int ch = -1;
     double tl = 0.0;
     if (W > 0.0) {
       const double target = u * W;
       double pre = 0.0;
       int last = -1;
-      for (int c = 0; c < nc; ++c) {
-        if (ds.E[c] > 0.0) last = c;
-        const double nxt = pre + ds.E[c];
-        if (nxt > target && ds.E[c] > 0.0) {
-          ch = c;
-          tl = target - pre;
+      for (int c0 = 0; c0 < nc; c0 += 64) {
+        const double e = (c0 + l < nc) ? ds.E[c0 + l] : 0.0;
+        const double sc = scan64_d(e);
+        const uint64_t pos = __ballot(e > 0.0);
+        if (pos) last = c0 + 63 - (int)__builtin_clzll(pos);
+        const uint64_t hit = __ballot(e > 0.0 && pre + sc > target);
+        if (hit) {
+          const int li = (int)__builtin_ctzll(hit);
+          ch = c0 + li;
+          tl = target - (li == 0 ? pre : pre + rl_d(sc, li - 1));
           break;
         }
-        pre = nxt;
+        pre += rl_d(sc, 63);
       }
       if (ch < 0) {   // rounding: target at or past the total
         ch = last;
         tl = POS_INF;
       }
     }
-    ds.chunk = ch;
-    ds.tl = tl;
+    if (l == 0) {
+      ds.chunk = ch;
+      ds.tl = tl;
+    }
   }
   __syncthreads();
   return ds.chunk >= 0;
