@@ -387,39 +387,6 @@ __device__ __forceinline__ double block_sum_d(double x, Smem& sm) {
   return r;
 }
 
-// Inclusive fp64 scan over the block in thread order; also returns the
-// exclusive value (the inclusive value of the previous thread).
-__device__ __forceinline__ void block_scan_d(double own, double& excl, double& incl, Smem& sm) {
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  double x = own;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  __syncthreads();
-  if (lane == 63) sm.d[w] = x;
-  __syncthreads();
-  double carry = 0.0;
-  for (int k = 0; k < w; ++k) carry += sm.d[k];
-  x += carry;
-  const double prev = __shfl_up(x, 1, 64);
-  incl = x;
-  excl = (lane == 0) ? carry : prev;
-}
-
-// The same scan, also returning the block total (the inclusive value of the
-// last thread, summed in the same order).
-__device__ __forceinline__ void block_scan_total_d(double own, double& excl, double& incl,
-                                                   double& total, Smem& sm) {
-  block_scan_d(own, excl, incl, sm);
-  double t = sm.d[0];
-#pragma unroll
-  for (int k = 1; k < NWAVE; ++k) t += sm.d[k];
-  total = t;
-}
-
 // A read-only input at an address that is the same in every lane, loaded
 // through the scalar cache: its wait counter is not the one of the vector
 // loads, so waiting for it never waits for the row data in flight.
@@ -545,6 +512,34 @@ __device__ __forceinline__ double scan32_d(double x) {
   x += dpp_or0_d<0x118, 0xf>(x);   // row_shr:8
   x += dpp_or0_d<0x142, 0x2>(x);   // row_bcast:15 into row 1
   return x;
+}
+
+// Inclusive fp64 scan over the block in thread order; also returns the
+// exclusive value (the inclusive value of the previous thread).
+__device__ __forceinline__ void block_scan_d(double own, double& excl, double& incl, Smem& sm) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  double x = scan64_d(own);   // within the wave (DPP)
+  __syncthreads();
+  if (lane == 63) sm.d[w] = x;
+  __syncthreads();
+  double carry = 0.0;
+  for (int k = 0; k < w; ++k) carry += sm.d[k];
+  x += carry;
+  const double prev = dpp_or0_d<0x138, 0xf>(x);   // wave_shr:1
+  incl = x;
+  excl = (lane == 0) ? carry : prev;
+}
+
+// The same scan, also returning the block total (the inclusive value of the
+// last thread, summed in the same order).
+__device__ __forceinline__ void block_scan_total_d(double own, double& excl, double& incl,
+                                                   double& total, Smem& sm) {
+  block_scan_d(own, excl, incl, sm);
+  double t = sm.d[0];
+#pragma unroll
+  for (int k = 1; k < NWAVE; ++k) t += sm.d[k];
+  total = t;
 }
 
 constexpr int DPP_XOR1 = 0xB1;      // quad_perm [1,0,3,2]
