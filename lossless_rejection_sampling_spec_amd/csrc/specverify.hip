@@ -335,58 +335,6 @@ struct Smem {
   unsigned long long u[NWAVE];
 };
 
-__device__ __forceinline__ float block_max(float x, Smem& sm) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmax3nan(x, __shfl_xor(x, o, 64));
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sm.f[w] = x;
-  __syncthreads();
-  float r = sm.f[0];
-#pragma unroll
-  for (int k = 1; k < NWAVE; ++k) r = fmax3nan(r, sm.f[k]);
-  return r;
-}
-
-__device__ __forceinline__ int block_min_i(int x, Smem& sm) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o, 64));
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sm.i[w] = x;
-  __syncthreads();
-  int r = sm.i[0];
-#pragma unroll
-  for (int k = 1; k < NWAVE; ++k) r = min(r, sm.i[k]);
-  return r;
-}
-
-__device__ __forceinline__ int block_max_i(int x, Smem& sm) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o, 64));
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sm.i[w] = x;
-  __syncthreads();
-  int r = sm.i[0];
-#pragma unroll
-  for (int k = 1; k < NWAVE; ++k) r = max(r, sm.i[k]);
-  return r;
-}
-
-__device__ __forceinline__ double block_sum_d(double x, Smem& sm) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sm.d[w] = x;
-  __syncthreads();
-  double r = sm.d[0];
-#pragma unroll
-  for (int k = 1; k < NWAVE; ++k) r += sm.d[k];
-  return r;
-}
-
 // A read-only input at an address that is the same in every lane, loaded
 // through the scalar cache: its wait counter is not the one of the vector
 // loads, so waiting for it never waits for the row data in flight.
@@ -514,6 +462,87 @@ __device__ __forceinline__ double scan32_d(double x) {
   return x;
 }
 
+constexpr int DPP_XOR1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int DPP_HMIRROR = 0x141;  // lane i <-> 7 - i within each 8
+constexpr int DPP_MIRROR = 0x140;   // lane i <-> 15 - i within each 16
+
+__device__ __forceinline__ float rl_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+__device__ __forceinline__ double rl_d(double x, int l) {
+  const long long v = __double_as_longlong(x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return __longlong_as_double((long long)(((u64)hi << 32) | lo));
+}
+
+template <int CTRL> __device__ __forceinline__ float dpp_any(float x) { return dpp_f<CTRL>(x); }
+template <int CTRL> __device__ __forceinline__ int dpp_any(int x) { return dpp_i<CTRL>(x); }
+template <int CTRL> __device__ __forceinline__ double dpp_any(double x) { return dpp_d<CTRL>(x); }
+__device__ __forceinline__ float rl_any(float x, int l) { return rl_f(x, l); }
+__device__ __forceinline__ int rl_any(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
+__device__ __forceinline__ double rl_any(double x, int l) { return rl_d(x, l); }
+
+// Block reductions: DPP within each 16-lane row, the four rows of a wave read
+// from lanes 0, 16, 32, 48, the waves through LDS in wave order.
+template <typename T, typename OP>
+__device__ __forceinline__ T wave_reduce_rows(T x, OP op) {
+  x = op(x, dpp_any<DPP_XOR1>(x));
+  x = op(x, dpp_any<DPP_XOR2>(x));
+  x = op(x, dpp_any<DPP_HMIRROR>(x));
+  x = op(x, dpp_any<DPP_MIRROR>(x));
+  return op(op(rl_any(x, 0), rl_any(x, 16)), op(rl_any(x, 32), rl_any(x, 48)));
+}
+
+__device__ __forceinline__ float block_max(float x, Smem& sm) {
+  x = wave_reduce_rows(x, [](float a, float b) { return fmax3nan(a, b); });
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sm.f[w] = x;
+  __syncthreads();
+  float r = sm.f[0];
+#pragma unroll
+  for (int k = 1; k < NWAVE; ++k) r = fmax3nan(r, sm.f[k]);
+  return r;
+}
+
+__device__ __forceinline__ int block_min_i(int x, Smem& sm) {
+  x = wave_reduce_rows(x, [](int a, int b) { return min(a, b); });
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sm.i[w] = x;
+  __syncthreads();
+  int r = sm.i[0];
+#pragma unroll
+  for (int k = 1; k < NWAVE; ++k) r = min(r, sm.i[k]);
+  return r;
+}
+
+__device__ __forceinline__ int block_max_i(int x, Smem& sm) {
+  x = wave_reduce_rows(x, [](int a, int b) { return max(a, b); });
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sm.i[w] = x;
+  __syncthreads();
+  int r = sm.i[0];
+#pragma unroll
+  for (int k = 1; k < NWAVE; ++k) r = max(r, sm.i[k]);
+  return r;
+}
+
+__device__ __forceinline__ double block_sum_d(double x, Smem& sm) {
+  x = wave_reduce_rows(x, [](double a, double b) { return a + b; });
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sm.d[w] = x;
+  __syncthreads();
+  double r = sm.d[0];
+#pragma unroll
+  for (int k = 1; k < NWAVE; ++k) r += sm.d[k];
+  return r;
+}
+
 // Inclusive fp64 scan over the block in thread order; also returns the
 // exclusive value (the inclusive value of the previous thread).
 __device__ __forceinline__ void block_scan_d(double own, double& excl, double& incl, Smem& sm) {
@@ -542,20 +571,6 @@ __device__ __forceinline__ void block_scan_total_d(double own, double& excl, dou
   total = t;
 }
 
-constexpr int DPP_XOR1 = 0xB1;      // quad_perm [1,0,3,2]
-constexpr int DPP_XOR2 = 0x4E;      // quad_perm [2,3,0,1]
-constexpr int DPP_HMIRROR = 0x141;  // lane i <-> 7 - i within each 8
-constexpr int DPP_MIRROR = 0x140;   // lane i <-> 15 - i within each 16
-
-__device__ __forceinline__ float rl_f(float x, int l) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
-}
-__device__ __forceinline__ double rl_d(double x, int l) {
-  const long long v = __double_as_longlong(x);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
-  return __longlong_as_double((long long)(((u64)hi << 32) | lo));
-}
 
 __device__ __forceinline__ float wave_max(float x) {
   x = fmax3nan(x, dpp_f<DPP_XOR1>(x));
@@ -1466,7 +1481,7 @@ __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, i
       }
     }
     block_scan_total_d(own, excl, incl, W, sm);
-    anybad = block_max_i(bad ? 1 : 0, sm);
+    anybad = logits ? 0 : block_max_i(bad ? 1 : 0, sm);   // logits are checked by the producers
   }
   const double u = (double)P.u[cu0 + k];
   if (nc <= PEER_MAX) {
