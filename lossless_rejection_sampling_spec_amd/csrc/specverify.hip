@@ -1107,6 +1107,7 @@ struct FinShared {
   int g[64];
   float lx[64], sx[64], dlx[64];
   int x[64];
+  float u[64];   // the request's uniforms, read with the draft ids
   int a, code, mode, timeout;
 };
 
@@ -1124,7 +1125,11 @@ __device__ __forceinline__ void finalize(const Params& P, int b, int cu0, int k,
   uint32_t* st_s = stage + (size_t)(2 * P.max_k + 1) * nc;
 
   if (tid == 0) fs.timeout = 0;
-  if (tid < 64) fs.x[tid] = (tid < k) ? P.drafts[d0 + tid] : -1;
+  if (tid < 64) {
+    fs.x[tid] = (tid < k) ? P.drafts[d0 + tid] : -1;
+    // uniforms exist for sampled requests only (the greedy entry passes none)
+    fs.u[tid] = (!R.greedy && tid <= k) ? P.u[cu0 + tid] : 0.f;
+  }
   __syncthreads();
   bool badtok_any = false;
   for (int i = 0; i < k; ++i) badtok_any |= (fs.x[i] < 0 || fs.x[i] >= P.vocab);
@@ -1271,7 +1276,7 @@ __device__ __forceinline__ void finalize(const Params& P, int b, int cu0, int k,
         } else {
           qx = 1.0;
         }
-        acc = (double)P.u[cu0 + j] * qx < px;
+        acc = (double)fs.u[j] * qx < px;
       }
     }
     const uint64_t m_nf = __ballot(nonfin);
@@ -1331,7 +1336,7 @@ __device__ __forceinline__ void finalize(const Params& P, int b, int cu0, int k,
       if (!(mrow[c] > NEG_INF)) return 0.0;
       return ex ? (double)(sxa * term(mrow[c], Ma, cf)) : (double)__uint_as_float(srow[c]);
     };
-    const int t = draw_target_row<TT, AL>(P, R, row, exclude, tau, (double)P.u[cu0 + k],
+    const int t = draw_target_row<TT, AL>(P, R, row, exclude, tau, (double)fs.u[k],
                                           [=](int c) { return mrow[c]; }, mass, rc, sm, ds);
     if (tid == 0) P.out[row] = t;
     if (has_helpers(P, R)) helpers_none(P, b);
@@ -1462,6 +1467,7 @@ __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, i
   Seg<TD> sq;
   load_contig<TT>(tp + c0, n, tvec, NEG_INF, sp);
   load_contig<TD>(dp + c0, n, dvec, qfill, sq);
+  const double u = (double)P.u[cu0 + k];   // arrives with the chunk
   // the chunk's residual mass as the total of a block scan of the segment
   // sums: the scan, the segment sums and the last positive elements are kept
   // for the draw, which then evaluates only the winning segment again
@@ -1483,7 +1489,6 @@ __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, i
     block_scan_total_d(own, excl, incl, W, sm);
     anybad = logits ? 0 : block_max_i(bad ? 1 : 0, sm);   // logits are checked by the producers
   }
-  const double u = (double)P.u[cu0 + k];
   if (nc <= PEER_MAX) {
     // every helper sends its chunk's mass to every other helper of the request
     // and takes theirs, so each picks the chunk itself; the one holding the
