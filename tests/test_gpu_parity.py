@@ -334,3 +334,20 @@ def test_residual_paths_around_the_peer_limit():
         _, c4 = check(synth.make(4, seed=5, batch=6, vocab=V))
         assert c2["match"] + c2["excused_accept"] + c2["excused_final"] >= 4
         assert c4["match"] + c4["excused_accept"] + c4["excused_final"] + c4["excused_near_tie"] == 6
+
+
+def test_draws_past_the_first_64_chunks():
+    """Rows of 74 chunks (V = 600,000): the chunk pick of a draw scans the chunk
+    masses 64 at a time; these seeds put the final token of a one-hot rejection
+    (the finalizer's draw), a draft-logit rejection and a probability-draft
+    rejection (the gathering helper's draw) in a chunk past the first 64."""
+    V = 600000
+    for cfg, seed, batch, req in ((2, 1, 8, 1), (2, 4, 8, 1), (4, 1, 6, 5)):
+        w = synth.make(cfg, seed=seed, batch=batch, vocab=V)
+        gpu, c = check(w)
+        assert c.get("fail", 0) == 0
+        cu = w.cu_seqlens
+        a = int(gpu["accepted"][req])
+        k = int(cu[req + 1] - cu[req] - 1)
+        assert 0 <= a < k, (cfg, seed, req, a, k)
+        assert int(gpu["out_tokens"][cu[req] + a]) >= 64 * 8192, (cfg, seed, req)
