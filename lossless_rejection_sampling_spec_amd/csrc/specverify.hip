@@ -360,14 +360,20 @@ struct Req {
 
 __device__ __forceinline__ Req load_req(const Params& P, int b) {
   Req R;
-  R.T = P.greedy_entry ? 0.f : ldu(P.temp + b);
+  // every load goes out at once (their conditions are kernel arguments only);
+  // the greedy test then selects what is kept
+  const float T = P.greedy_entry ? 0.f : ldu(P.temp + b);
+  const int kind = P.greedy_entry ? -1 : ldu(P.kind + b);
+  const int K = P.top_k ? ldu(P.top_k + b) : 0;
+  const float Pp = P.top_p ? ldu(P.top_p + b) : 1.f;
+  R.T = T;
   R.greedy = P.greedy_entry || !(R.T >= FLT_MIN);
-  R.kind = R.greedy ? -1 : ldu(P.kind + b);
+  R.kind = R.greedy ? -1 : kind;
   R.bad_param = !R.greedy &&
                 (R.T == POS_INF || R.kind < SV_DRAFT_ONEHOT || R.kind > SV_DRAFT_PROBS ||
                  (R.kind != SV_DRAFT_ONEHOT && P.draft == nullptr));
-  R.K = (!R.greedy && P.top_k) ? ldu(P.top_k + b) : 0;
-  R.P = (!R.greedy && P.top_p) ? ldu(P.top_p + b) : 1.f;
+  R.K = R.greedy ? 0 : K;
+  R.P = R.greedy ? 1.f : Pp;
   if (R.K >= P.vocab) R.K = 0;
   R.filt = R.K > 0 || (R.P > 0.f && R.P < 1.f);
   if (!R.greedy && !R.bad_param) {
@@ -808,11 +814,16 @@ __device__ __forceinline__ void produce(const Params& P, const Req& R, int b, in
   const int row = cu0 + j;
   const int d0 = cu0 - b;
   const TT* trow = (const TT*)P.target + (int64_t)row * P.ld_t;
-  const float tau = (P.thr_t && R.filt) ? thr_of(P.thr_t, row) : NEG_INF;
+  // the draft id and the thresholds are loaded without waiting for the
+  // request's parameters, which only decide whether they are used
+  const int xr = j < k ? ldu(P.drafts + d0 + j) : -1;
+  const float tau_r = P.thr_t ? thr_of(P.thr_t, row) : NEG_INF;
+  const float taud_r = (P.thr_d && j < k) ? thr_of(P.thr_d, d0 + j) : NEG_INF;
+  const float tau = R.filt ? tau_r : NEG_INF;
   const bool has_d = R.kind == SV_DRAFT_LOGITS && j < k;
   const TD* drow = (const TD*)P.draft + (int64_t)(d0 + j) * P.ld_d;
-  const float taud = (has_d && P.thr_d && R.filt) ? thr_of(P.thr_d, d0 + j) : NEG_INF;
-  const int x = (!R.greedy && j < k) ? ldu(P.drafts + d0 + j) : -1;
+  const float taud = (has_d && R.filt) ? taud_r : NEG_INF;
+  const int x = R.greedy ? -1 : xr;
   const int c_begin = s * P.S;
   const int c_end = min(c_begin + P.S, nc);
   const int sh = has_d ? 1 : 0;   // task t: chunk c_begin + (t >> sh), draft iff t & sh
