@@ -963,19 +963,20 @@ __device__ __forceinline__ int draw_scanned(const Seg<TA>& sa, const Seg<TB>& sb
   return ds.tok;
 }
 
-// Weight sum of this thread's segment, in element order (the order the draw's
-// scan assumes).
+// Weight sum of this thread's segment (its interval in the draw's block scan).
 template <typename TA, typename TB, bool TWO, typename WF>
 __device__ __forceinline__ double seg_weights(const Seg<TA>& sa, const Seg<TB>& sb, int c0,
                                               WF weight) {
   const int seg = threadIdx.x * EPT;
-  double own = 0.0;
+  // two partial sums (even and odd elements) halve the chain of dependent adds
+  double own0 = 0.0, own1 = 0.0;
 #pragma unroll
-  for (int i = 0; i < EPT; ++i) {
-    own += weight(sa.at(i), TWO ? sb.at(i) : 0.f, c0 + seg + i);
-    if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound live fp64 temporaries
+  for (int i = 0; i < EPT; i += 2) {
+    own0 += weight(sa.at(i), TWO ? sb.at(i) : 0.f, c0 + seg + i);
+    own1 += weight(sa.at(i + 1), TWO ? sb.at(i + 1) : 0.f, c0 + seg + i + 1);
+    if ((i & 3) == 2) __builtin_amdgcn_sched_barrier(0);   // bound live fp64 temporaries
   }
-  return own;
+  return own0 + own1;
 }
 
 // The draw over a chunk whose segment sums are not known yet.
@@ -1471,7 +1472,7 @@ __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, i
   double W;
   int anybad;
   ResCtx X;
-  res_ctx(P, R, su, cmp, cmq, trow, drow, X);
+  // the chunk is requested first; the weights' context is computed while it loads
   const int c0 = c * CHUNK;
   const int n = min(CHUNK, P.vocab - c0);
   Seg<TT> sp;
@@ -1479,6 +1480,7 @@ __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, i
   load_contig<TT>(tp + c0, n, tvec, NEG_INF, sp);
   load_contig<TD>(dp + c0, n, dvec, qfill, sq);
   const double u = (double)P.u[cu0 + k];   // arrives with the chunk
+  res_ctx(P, R, su, cmp, cmq, trow, drow, X);
   // the chunk's residual mass as the total of a block scan of the segment
   // sums: the scan, the segment sums and the last positive elements are kept
   // for the draw, which then evaluates only the winning segment again
