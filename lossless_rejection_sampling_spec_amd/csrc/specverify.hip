@@ -93,9 +93,11 @@ constexpr int PEER_MAX = 32;
 
 typedef unsigned long long u64;
 
-// What a helper learns from its decision record (plain data).  Every 32-bit
-// value of the workspace sits in the low half of a 64-bit word, so no word ever
-// has its top ("fresh") bit set unless it is a hand-off word in flight.
+// What a helper learns from its decision record (plain data).  No value of the
+// workspace sets the top ("fresh") bit of its 64-bit word: 32-bit values sit in
+// the low half, and the chunk statistics keep their never-negative sum or
+// argmax in the high half below that bit, so only a hand-off word in flight
+// has it set.
 struct Setup {
   double Sp, Sq;
   float Mp, Mq;
