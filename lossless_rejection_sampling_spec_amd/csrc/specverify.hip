@@ -515,18 +515,6 @@ __device__ __forceinline__ float block_max(float x, Smem& sm) {
   return r;
 }
 
-__device__ __forceinline__ int block_min_i(int x, Smem& sm) {
-  x = wave_reduce_rows(x, [](int a, int b) { return min(a, b); });
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sm.i[w] = x;
-  __syncthreads();
-  int r = sm.i[0];
-#pragma unroll
-  for (int k = 1; k < NWAVE; ++k) r = min(r, sm.i[k]);
-  return r;
-}
-
 __device__ __forceinline__ int block_max_i(int x, Smem& sm) {
   x = wave_reduce_rows(x, [](int a, int b) { return max(a, b); });
   const int w = threadIdx.x >> 6;
