@@ -6,10 +6,14 @@
 // bandwidth-bound stream over vocabulary rows).
 //
 // One fused kernel, k_verify, does the whole verify of a batch:
+//   draft       (sampled calls with draft rows) launched first: workgroup
+//   strips      (b, j, s) reads a strip of S chunks of draft row j of a
+//               draft-logit request once from HBM and publishes per-chunk
+//               statistics (max, sum of exp2 terms).
 //   producers   workgroup (b, j, s) reads a strip of S chunks (CHUNK elements
-//               each) of target row j of request b -- and of draft row j when
-//               the request's drafts are logits -- once from HBM and publishes
-//               per-chunk statistics (max, sum of exp2 terms, or argmax).
+//               each) of target row j of request b once from HBM and
+//               publishes per-chunk statistics (max, sum of exp2 terms, or
+//               argmax) and the values at the draft id.
 //   finalizer   the last producer of a request in launch order waits for the
 //               request's statistics, merges them in a fixed order, runs the
 //               acceptance scan as a 64-lane ballot (lane j = position j),
@@ -31,8 +35,8 @@
 // the word with one agent-scope atomic store (coherent across the eight XCD
 // L2 caches, no fence, no counter), the single reader of that word waits for
 // the tag, takes the payload and stores the word back without its tag.
-// Producers wait for nothing; finalizers wait for producers launched before
-// them; helpers wait for their finalizer and for the other helpers of the
+// Draft strips and producers wait for nothing; finalizers wait for draft
+// strips and producers launched before them; helpers wait for their finalizer and for the other helpers of the
 // same request, which are launched together (see helper()).  Every wait is
 // bounded (a request whose wait runs out reports SV_ROW_INTERNAL).  A
 // workspace is therefore left with no tag set when a call ends.
@@ -133,6 +137,7 @@ struct Params {
   int ns;         // strips per row
   int H;          // helper workgroups per request (nc, or 0 for the greedy entry)
   int greedy_entry;
+  int dsplit;     // draft-logit rows are read by draft strips of their own
 };
 
 // ---------------------------------------------------------------------------
@@ -791,12 +796,10 @@ __device__ __forceinline__ void produce_task(const Params& P, const Req& R, cons
   }
 }
 
-// Producer of request b, row j, strip s: statistics of S chunks of the target
-// row (and of the draft row for draft-logit requests).  The tasks (a target
-// chunk, then the draft chunk when there is one) run through two buffers: the
-// loads of task t+1 are issued before task t is reduced.  Every step issues
-// a load (the last task's is repeated) so the wait before each reduction only
-// covers the buffer it reads; the hand-off words are written after the strip.
+// Producer of request b, target row j, strip s: statistics of S chunks of the
+// target row, and the single values at the draft id when it falls in the
+// strip.  Draft rows are read by draft strips of their own (produce_draft).
+// The hand-off words are written after the strip.
 template <typename TT, typename TD, bool AL>
 __device__ __forceinline__ void produce(const Params& P, const Req& R, int b, int cu0, int k,
                                         int j, int s, ProdShared& ps, Buf<TT, TD>& A) {
@@ -810,14 +813,12 @@ __device__ __forceinline__ void produce(const Params& P, const Req& R, int b, in
   const float tau_r = P.thr_t ? thr_of(P.thr_t, row) : NEG_INF;
   const float taud_r = (P.thr_d && j < k) ? thr_of(P.thr_d, d0 + j) : NEG_INF;
   const float tau = R.filt ? tau_r : NEG_INF;
-  const bool has_d = R.kind == SV_DRAFT_LOGITS && j < k;
   const TD* drow = (const TD*)P.draft + (int64_t)(d0 + j) * P.ld_d;
-  const float taud = (has_d && R.filt) ? taud_r : NEG_INF;
+  const float taud = (R.kind == SV_DRAFT_LOGITS && j < k && R.filt) ? taud_r : NEG_INF;
   const int x = R.greedy ? -1 : xr;
   const int c_begin = s * P.S;
   const int c_end = min(c_begin + P.S, nc);
-  const int sh = has_d ? 1 : 0;   // task t: chunk c_begin + (t >> sh), draft iff t & sh
-  const int nt = (c_end - c_begin) << sh;
+  const int nt = c_end - c_begin;
   // the single values at the draft id, gathered by thread 0 and published
   // after the strip (issued first, they wait behind nothing)
   const bool xs = threadIdx.x == 0 && x >= c_begin * CHUNK && x < min(c_end * CHUNK, P.vocab);
@@ -828,53 +829,29 @@ __device__ __forceinline__ void produce(const Params& P, const Req& R, int b, in
     if (R.kind != SV_DRAFT_ONEHOT) ldx_raw = drow[x];
   }
 
-  if (!has_d) {
-    // target chunks only, two in flight: chunk t+1 is requested before chunk t
-    // is reduced.  Past the row's last chunk the loads repeat it (never
-    // reduced).  Two chunks per workgroup keep the memory busy with every slot
-    // of the GPU filled, and fewer bytes queued ahead of every load shorten the
-    // dependent round trips that follow the statistics.
-    constexpr int S = Strip<TT>::S;
-    Buf<TT, TD> Q[S];
-    Q[0] = A;
+  // two chunks in flight: chunk t+1 is requested before chunk t is reduced.
+  // Past the row's last chunk the loads repeat it (never reduced).  Two
+  // chunks per workgroup keep the memory busy with every slot of the GPU
+  // filled, and fewer bytes queued ahead of every load shorten the dependent
+  // round trips that follow the statistics.
+  constexpr int S = Strip<TT>::S;
+  Buf<TT, TD> Q[S];
+  Q[0] = A;
 #pragma unroll
-    for (int t = 0; t < S; ++t) {
-      if (t + 1 < S)
-        issue_task<TT, TD, AL>(trow, drow, false, c_begin + min(t + 1, nt - 1), P.vocab, Q[t + 1]);
-      if (t < nt) produce_task<TT, TT, TD, AL>(P, R, Q[t], false, c_begin + t, x, tau, t, ps);
-    }
-  } else {
-  Buf<TT, TD> B;   // A holds the first task's loads (issued by the caller)
-  int t = 0;
-  for (; t + 1 < nt; t += 2) {
-    const int t1 = t + 1;
-    issue_task<TT, TD, AL>(trow, drow, (t1 & sh) != 0, c_begin + (t1 >> sh), P.vocab, B);
-    if ((t & sh) == 0)
-      produce_task<TT, TT, TD, AL>(P, R, A, false, c_begin + (t >> sh), x, tau, t, ps);
-    else
-      produce_task<TD, TT, TD, AL>(P, R, A, true, c_begin + (t >> sh), x, taud, t, ps);
-    const int t2 = min(t + 2, nt - 1);
-    issue_task<TT, TD, AL>(trow, drow, (t2 & sh) != 0, c_begin + (t2 >> sh), P.vocab, A);
-    if ((t1 & sh) == 0)
-      produce_task<TT, TT, TD, AL>(P, R, B, false, c_begin + (t1 >> sh), x, tau, t1, ps);
-    else
-      produce_task<TD, TT, TD, AL>(P, R, B, true, c_begin + (t1 >> sh), x, taud, t1, ps);
-  }
-  if (t < nt) {   // odd count: the last task is a target chunk, already in A
-    produce_task<TT, TT, TD, AL>(P, R, A, false, c_begin + (t >> sh), x, tau, t, ps);
-  }
+  for (int t = 0; t < S; ++t) {
+    if (t + 1 < S)
+      issue_task<TT, TD, AL>(trow, drow, false, c_begin + min(t + 1, nt - 1), P.vocab, Q[t + 1]);
+    if (t < nt) produce_task<TT, TT, TD, AL>(P, R, Q[t], false, c_begin + t, x, tau, t, ps);
   }
   __syncthreads();
   const int tp = threadIdx.x;
   if (tp < nt) {
-    const bool is_d = (tp & sh) != 0;
-    const int c = c_begin + (tp >> sh);
+    const int c = c_begin + tp;
     // one word per chunk: the sum (or argmax) is never negative, so its top
     // bit is free for the tag
-    u64* w = is_d ? P.dst + ((int64_t)(d0 + j) * nc + c) : P.cst + ((int64_t)row * nc + c);
-    put_w(w, ps.pub[tp][1] & ~TAG, ps.pub[tp][0]);
+    put_w(P.cst + ((int64_t)row * nc + c), ps.pub[tp][1] & ~TAG, ps.pub[tp][0]);
     const int c0 = c * CHUNK;
-    if (!is_d && x >= c0 && x < c0 + min(CHUNK, P.vocab - c0))
+    if (x >= c0 && x < c0 + min(CHUNK, P.vocab - c0))
       put_w(P.rx + (int64_t)row * 3 + 1, 0u, ps.pub[tp][2]);
   }
   if (xs) {
@@ -888,6 +865,37 @@ __device__ __forceinline__ void produce(const Params& P, const Req& R, int b, in
       put_w(P.rx + (int64_t)row * 3 + 2, 0u, __float_as_uint(ldx));
     }
   }
+}
+
+// Draft strip of request b, draft row j, strip s (draft-logit requests): the
+// statistics of S chunks of the draft row, two chunks in flight, published to
+// the draft hand-off words.  Draft strips come first in the grid, so the draft
+// rows stream while the target strips start, with the same bytes per
+// workgroup.
+template <typename TT, typename TD, bool AL>
+__device__ __forceinline__ void produce_draft(const Params& P, const Req& R, int b, int cu0, int j,
+                                              int s, ProdShared& ps, Buf<TT, TD>& A) {
+  const int nc = P.nc;
+  const int d0 = cu0 - b;
+  const TD* drow = (const TD*)P.draft + (int64_t)(d0 + j) * P.ld_d;
+  const float taud_r = P.thr_d ? thr_of(P.thr_d, d0 + j) : NEG_INF;
+  const float taud = R.filt ? taud_r : NEG_INF;
+  const int c_begin = s * P.S;
+  const int c_end = min(c_begin + P.S, nc);
+  const int nt = c_end - c_begin;
+  constexpr int S = Strip<TT>::S;
+  Buf<TT, TD> Q[S];
+  Q[0] = A;
+#pragma unroll
+  for (int t = 0; t < S; ++t) {
+    if (t + 1 < S)
+      issue_task<TT, TD, AL>((const TT*)nullptr, drow, true, c_begin + min(t + 1, nt - 1), P.vocab, Q[t + 1]);
+    if (t < nt) produce_task<TD, TT, TD, AL>(P, R, Q[t], true, c_begin + t, -1, taud, t, ps);
+  }
+  __syncthreads();
+  const int tp = threadIdx.x;
+  if (tp < nt)
+    put_w(P.dst + ((int64_t)(d0 + j) * nc + c_begin + tp), ps.pub[tp][1] & ~TAG, ps.pub[tp][0]);
 }
 
 // ---------------------------------------------------------------------------
@@ -1648,6 +1656,7 @@ __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, i
 struct ReqPos {
   int b, cu0, cu1;
   int cls;        // launch class: 0 sampled with draft rows, 1 other sampled, 2 greedy
+  bool dlog;      // the draft rows are logits
   bool valid;
 };
 
@@ -1675,9 +1684,11 @@ __device__ __forceinline__ ReqPos req_at(const Params& P, int pos) {
   const int lane = threadIdx.x & 63;
   const int B = P.batch;
   const int i0 = lane * E;
-  int lo[E + 1], cl[E];
+  int lo[E + 1], cl[E], lg[E];
 #pragma unroll
   for (int e = 0; e <= E; ++e) lo[e] = P.cu[min(i0 + e, B)];
+#pragma unroll
+  for (int e = 0; e < E; ++e) lg[e] = 0;
   if (!P.greedy_entry) {
     float T[E];
     int kd[E];
@@ -1691,6 +1702,8 @@ __device__ __forceinline__ ReqPos req_at(const Params& P, int pos) {
     for (int e = 0; e < E; ++e)
       cl[e] = (i0 + e >= B) ? 3 : !(T[e] >= FLT_MIN) ? 2
               : (kd[e] == SV_DRAFT_LOGITS || kd[e] == SV_DRAFT_PROBS) ? 0 : 1;
+#pragma unroll
+    for (int e = 0; e < E; ++e) lg[e] = kd[e] == SV_DRAFT_LOGITS;
   } else {
 #pragma unroll
     for (int e = 0; e < E; ++e) cl[e] = (i0 + e >= B) ? 3 : 2;
@@ -1729,12 +1742,13 @@ __device__ __forceinline__ ReqPos req_at(const Params& P, int pos) {
   const int minc = wave_scan_max(mloc);
   const int before = __builtin_amdgcn_update_dpp(INT32_MIN, minc, 0x138, 0xf, 0xf, false);  // wave_shr:1
   run_at = max(run_at, before);
-  int c_lo = 0, c_hi = 0;
+  int c_lo = 0, c_hi = 0, g = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     if (e == ei) {
       c_lo = lo[e];
       c_hi = lo[e + 1];
+      g = lg[e];
     }
   }
   const uint64_t m = __ballot(mine);
@@ -1745,6 +1759,7 @@ __device__ __forceinline__ ReqPos req_at(const Params& P, int pos) {
   R.cu1 = __builtin_amdgcn_readlane(c_hi, src);
   const int ra = __builtin_amdgcn_readlane(run_at, src);
   R.cls = tc;
+  R.dlog = __builtin_amdgcn_readlane(g, src) != 0;
   R.valid = R.cu0 >= ra && req_valid(P, R.b, R.cu0, R.cu1, R.cu1 - R.cu0 - 1);
   return R;
 }
@@ -1758,7 +1773,28 @@ __global__ __launch_bounds__(WG, 4) void k_verify(const Params P) {
   __shared__ ProdShared ps;
   extern __shared__ uint32_t stage[];
   const int Pw = (P.max_k + 1) * P.ns;
-  const long long id = blockIdx.x;
+  long long id = blockIdx.x;
+  if (P.dsplit) {   // draft strips first
+    const long long nd = (long long)P.batch * P.max_k * P.ns;
+    if (id < nd) {
+      const int Pd = P.max_k * P.ns;
+      const int per = (int)(id / Pd);
+      const int loc = (int)(id - (long long)per * Pd);
+      const int j = loc / P.ns;
+      const int s = loc - j * P.ns;
+      const ReqPos Q = req_at<E>(P, per);
+      if (!Q.valid || Q.cls != 0 || !Q.dlog) return;
+      const int k = Q.cu1 - Q.cu0 - 1;
+      if (j >= k) return;
+      Buf<TT, TD> A;
+      issue_task<TT, TD, AL>((const TT*)nullptr, (const TD*)P.draft + (int64_t)(Q.cu0 - Q.b + j) * P.ld_d,
+                             true, s * P.S, P.vocab, A);
+      const Req R = load_req(P, Q.b);
+      if (!R.bad_param && R.kind == SV_DRAFT_LOGITS) produce_draft<TT, TD, AL>(P, R, Q.b, Q.cu0, j, s, ps, A);
+      return;
+    }
+    id -= nd;
+  }
   const long long np = (long long)P.batch * Pw;   // producer workgroups
   if (id >= np) {   // helper of the request at position hpos, chunk c
     const int hpos = (int)((id - np) / P.H);
@@ -1988,7 +2024,8 @@ static bool layout(int batch, int total_rows, int vocab, int max_k, Layout& L, i
 
 template <typename TT>
 static long long verify_grid(const Params& P) {
-  return (long long)P.batch * (P.max_k + 1) * P.ns + (long long)P.batch * P.H;
+  return (long long)P.batch * (P.max_k + 1) * P.ns + (long long)P.batch * P.H +
+         (P.dsplit ? (long long)P.batch * P.max_k * P.ns : 0);
 }
 
 template <typename TT, typename TD>
@@ -1996,6 +2033,7 @@ static int launch_all(Params P, bool sampled, bool filters, bool aligned, hipStr
   P.S = Strip<TT>::S;   // at most 8: a strip's statistics fit ProdShared::pub
   P.ns = (P.nc + P.S - 1) / P.S;
   P.H = sampled ? P.nc : 0;
+  P.dsplit = (sampled && P.draft != nullptr) ? 1 : 0;
   const long long g = verify_grid<TT>(P);
   if (g >= (1LL << 31)) return SV_ERR_SHAPE;
   const size_t lds = (size_t)8 * (2 * P.max_k + 1) * P.nc;
