@@ -36,8 +36,8 @@ KERNEL_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)),
 # the SHA-256 of the kernel source the counters were taken on: for any other
 # source the figure is stale and the bench reports null.
 TRAFFIC_BYTES = {
-    # 71819.6 KiB fetched x 1.99919, 343.1 KiB written: 1.056x the algorithmic bytes
-    "8b082a313734cfa23943c4b53de7fb70b0ee5c7d2a3bef6b8c7aa668452fc085": 147378187,
+    # 71815.3 KiB fetched x 1.99920, 344.1 KiB written: 1.056x the algorithmic bytes
+    "528bdad96d9c23657336e21587965a857488b1d75127f9e31ce02ac113981ae7": 147371247,
 }
 
 

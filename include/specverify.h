@@ -36,17 +36,20 @@
  *   - target rows   cu[b] .. cu[b] + k_b          (row j scores position j)
  *   - draft rows and draft tokens  cu[b]-b .. cu[b]-b+k_b-1
  *   - uniforms u[cu[b] + i]: i < k_b acceptance draws, i = k_b the final draw
- *   total_rows = cu[batch]; cu must be non-decreasing with cu[0] = 0 (a request
- *   whose first offset is below an earlier one is reported BAD_K, so the rows
- *   of the requests that are verified never overlap).
+ *   total_rows = cu[batch]; cu must be non-decreasing with cu[0] = 0 and every
+ *   k_b >= 0.  A request whose first target row cu[b] is below an earlier
+ *   request's, or whose first draft row cu[b]-b is below an earlier request's
+ *   cu[e]-e, is reported BAD_K (after a request with no rows, or offsets that go
+ *   back, the next draft rows would reach into an earlier request's), so neither
+ *   the target rows nor the draft rows of the requests that are verified overlap.
  * Layouts: logit / probability buffers are row-major [rows, ld] with ld >= vocab
  *   elements; only the first `vocab` entries of a row are read.  Rows whose
  *   address is 16-byte aligned take 128-bit loads, others a scalar path.
  * Values: -inf in a logit row masks that token.  NaN or +inf in a needed logit
  *   row, or a NaN/inf/negative needed probability, is a data fault.
  * Per-request status (status[b]) is written on the device; first match wins:
- *   SV_ROW_BAD_K     offsets out of range, k_b < 0, k_b > max_k, or cu[b] below
- *                    an earlier offset
+ *   SV_ROW_BAD_K     offsets out of range, k_b < 0, k_b > max_k, cu[b] below
+ *                    an earlier offset, or cu[b]-b below an earlier cu[e]-e
  *   SV_ROW_BAD_PARAM unknown draft kind, a kind that needs draft rows with a
  *                    NULL draft buffer, or temperature +inf
  *   SV_ROW_BAD_TOKEN a draft id outside [0, vocab)

@@ -1651,12 +1651,19 @@ __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, i
 // consecutive requests per lane (E = 1 for batches of up to 64, else 16),
 // their offsets, temperatures and draft kinds loaded together (one round trip,
 // indices clamped into the batch), classes counted by ballots and DPP scans.
-// A request is valid when its offsets pass req_valid and its first offset is
-// not below any earlier one (the rows of valid requests never overlap).
+// A request is valid when its offsets pass req_valid and its first draft row
+// cu[b] - b is not below any earlier request's cu[e] - e.  That also puts cu[b]
+// above every earlier offset, so neither the target rows nor the draft rows of
+// valid requests overlap (an earlier request with no rows, or offsets that go
+// back, would otherwise let the next draft rows reach into an earlier
+// request's, and two requests would publish to the same hand-off words).
+__device__ __forceinline__ int first_drow(int cu_i, int i) {   // cu[i] - i, clamped
+  return (int)max((long long)cu_i - i, (long long)INT32_MIN);
+}
+
 struct ReqPos {
   int b, cu0, cu1;
   int cls;        // launch class: 0 sampled with draft rows, 1 other sampled, 2 greedy
-  bool dlog;      // the draft rows are logits
   bool valid;
 };
 
@@ -1684,11 +1691,9 @@ __device__ __forceinline__ ReqPos req_at(const Params& P, int pos) {
   const int lane = threadIdx.x & 63;
   const int B = P.batch;
   const int i0 = lane * E;
-  int lo[E + 1], cl[E], lg[E];
+  int lo[E + 1], cl[E];
 #pragma unroll
   for (int e = 0; e <= E; ++e) lo[e] = P.cu[min(i0 + e, B)];
-#pragma unroll
-  for (int e = 0; e < E; ++e) lg[e] = 0;
   if (!P.greedy_entry) {
     float T[E];
     int kd[E];
@@ -1702,8 +1707,6 @@ __device__ __forceinline__ ReqPos req_at(const Params& P, int pos) {
     for (int e = 0; e < E; ++e)
       cl[e] = (i0 + e >= B) ? 3 : !(T[e] >= FLT_MIN) ? 2
               : (kd[e] == SV_DRAFT_LOGITS || kd[e] == SV_DRAFT_PROBS) ? 0 : 1;
-#pragma unroll
-    for (int e = 0; e < E; ++e) lg[e] = kd[e] == SV_DRAFT_LOGITS;
   } else {
 #pragma unroll
     for (int e = 0; e < E; ++e) cl[e] = (i0 + e >= B) ? 3 : 2;
@@ -1732,23 +1735,23 @@ __device__ __forceinline__ ReqPos req_at(const Params& P, int pos) {
       ++seen;
     }
   }
-  // offsets must not go back: the running max of cu[0..i-1] at that entry
+  // offsets must not go back: the running max of cu[i] - i over the requests
+  // before that entry
   int mloc = INT32_MIN, run_at = INT32_MIN;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     if (e == ei) run_at = mloc;
-    mloc = (i0 + e < B) ? max(mloc, lo[e]) : mloc;
+    mloc = (i0 + e < B) ? max(mloc, first_drow(lo[e], i0 + e)) : mloc;
   }
   const int minc = wave_scan_max(mloc);
   const int before = __builtin_amdgcn_update_dpp(INT32_MIN, minc, 0x138, 0xf, 0xf, false);  // wave_shr:1
   run_at = max(run_at, before);
-  int c_lo = 0, c_hi = 0, g = 0;
+  int c_lo = 0, c_hi = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     if (e == ei) {
       c_lo = lo[e];
       c_hi = lo[e + 1];
-      g = lg[e];
     }
   }
   const uint64_t m = __ballot(mine);
@@ -1759,9 +1762,23 @@ __device__ __forceinline__ ReqPos req_at(const Params& P, int pos) {
   R.cu1 = __builtin_amdgcn_readlane(c_hi, src);
   const int ra = __builtin_amdgcn_readlane(run_at, src);
   R.cls = tc;
-  R.dlog = __builtin_amdgcn_readlane(g, src) != 0;
-  R.valid = R.cu0 >= ra && req_valid(P, R.b, R.cu0, R.cu1, R.cu1 - R.cu0 - 1);
+  R.valid = R.cu0 >= 0 && R.cu0 - R.b >= ra && req_valid(P, R.b, R.cu0, R.cu1, R.cu1 - R.cu0 - 1);
   return R;
+}
+
+// Whether request b's offsets are valid, the verdict req_at gives for it: one
+// wave-level load of the offsets for the largest cu[i] - i before b.
+template <int E>
+__device__ __forceinline__ bool offsets_ok(const Params& P, int b, int cu0, int cu1) {
+  const int i0 = (threadIdx.x & 63) * E;
+  int m = INT32_MIN;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int v = P.cu[min(i0 + e, P.batch)];
+    if (i0 + e < b) m = max(m, first_drow(v, i0 + e));
+  }
+  const int ra = __builtin_amdgcn_readlane(wave_scan_max(m), 63);
+  return cu0 >= 0 && cu0 - b >= ra && req_valid(P, b, cu0, cu1, cu1 - cu0 - 1);
 }
 
 template <typename TT, typename TD, bool AL, int E>
@@ -1778,19 +1795,20 @@ __global__ __launch_bounds__(WG, 4) void k_verify(const Params P) {
     const long long nd = (long long)P.batch * P.max_k * P.ns;
     if (id < nd) {
       const int Pd = P.max_k * P.ns;
-      const int per = (int)(id / Pd);
-      const int loc = (int)(id - (long long)per * Pd);
+      const int b = (int)(id / Pd);
+      const int loc = (int)(id - (long long)b * Pd);
       const int j = loc / P.ns;
       const int s = loc - j * P.ns;
-      const ReqPos Q = req_at<E>(P, per);
-      if (!Q.valid || Q.cls != 0 || !Q.dlog) return;
-      const int k = Q.cu1 - Q.cu0 - 1;
-      if (j >= k) return;
+      // scalar loads decide which requests have draft-logit rows; only those
+      // pay the vector lookup that checks the offsets
+      const Req R = load_req(P, b);
+      const int cu0 = ldu(P.cu + b), cu1 = ldu(P.cu + b + 1);
+      if (R.greedy || R.bad_param || R.kind != SV_DRAFT_LOGITS || j >= cu1 - cu0 - 1) return;
+      if (!offsets_ok<E>(P, b, cu0, cu1)) return;
       Buf<TT, TD> A;
-      issue_task<TT, TD, AL>((const TT*)nullptr, (const TD*)P.draft + (int64_t)(Q.cu0 - Q.b + j) * P.ld_d,
+      issue_task<TT, TD, AL>((const TT*)nullptr, (const TD*)P.draft + (int64_t)(cu0 - b + j) * P.ld_d,
                              true, s * P.S, P.vocab, A);
-      const Req R = load_req(P, Q.b);
-      if (!R.bad_param && R.kind == SV_DRAFT_LOGITS) produce_draft<TT, TD, AL>(P, R, Q.b, Q.cu0, j, s, ps, A);
+      produce_draft<TT, TD, AL>(P, R, b, cu0, j, s, ps, A);
       return;
     }
     id -= nd;
@@ -1959,7 +1977,7 @@ __device__ float row_threshold(const T* __restrict__ rp, int V, int levels, cons
   return keyf(tau_key);
 }
 
-template <typename TT, typename TD>
+template <typename TT, typename TD, int E>
 __global__ __launch_bounds__(WG) void k_thresh(const Params P) {
   __shared__ Smem sm;
   __shared__ ThrShared th;
@@ -1971,7 +1989,8 @@ __global__ __launch_bounds__(WG) void k_thresh(const Params P) {
   const int cu0 = P.cu[b];
   const int cu1 = P.cu[b + 1];
   const int k = cu1 - cu0 - 1;
-  if (!req_valid(P, b, cu0, cu1, k) || j > k) return;
+  // the verdict k_verify gives: rows of an invalid request may be another's
+  if (j > k || !offsets_ok<E>(P, b, cu0, cu1)) return;
   const Req R = load_req(P, b);
   if (R.greedy || R.bad_param || !R.filt) return;
   if (side == 1 && (R.kind != SV_DRAFT_LOGITS || j >= k)) return;
@@ -2037,11 +2056,15 @@ static int launch_all(Params P, bool sampled, bool filters, bool aligned, hipStr
   const long long g = verify_grid<TT>(P);
   if (g >= (1LL << 31)) return SV_ERR_SHAPE;
   const size_t lds = (size_t)8 * (2 * P.max_k + 1) * P.nc;
+  // requests per lane when finding a request by launch position or checking
+  // its offsets
   if (filters) {
     const long long g0 = (long long)P.batch * (P.max_k + 1) * 2;
-    hipLaunchKernelGGL((k_thresh<TT, TD>), dim3((unsigned)g0), dim3(WG), 0, st, P);
+    if (P.batch <= 64)
+      hipLaunchKernelGGL((k_thresh<TT, TD, 1>), dim3((unsigned)g0), dim3(WG), 0, st, P);
+    else
+      hipLaunchKernelGGL((k_thresh<TT, TD, 16>), dim3((unsigned)g0), dim3(WG), 0, st, P);
   }
-  // requests per lane when finding a request by launch position
   if (P.batch <= 64) {
     if (aligned)
       hipLaunchKernelGGL((k_verify<TT, TD, true, 1>), dim3((unsigned)g), dim3(WG), lds, st, P);

@@ -307,13 +307,18 @@ def request_bounds(cu, b: int, batch: int, total_rows: int, max_k: int):
     """(k, valid) of request b from the cu_seqlens offsets: the request owns
     target rows cu[b]..cu[b+1]-1 and draft rows cu[b]-b .. cu[b+1]-b-2.
 
-    Offsets must be non-decreasing: a request whose first offset is below an
-    earlier offset is invalid, so the rows of valid requests never overlap."""
+    Offsets must be non-decreasing: a request is invalid when its first target
+    row cu[b] is below an earlier request's, or its first draft row cu[b]-b is
+    below an earlier request's cu[e]-e (after a request with no rows, or with
+    offsets that go back, the draft rows that follow would reach back into an
+    earlier request's).  So neither the target rows nor the draft rows of
+    valid requests overlap."""
     c0, c1 = int(cu[b]), int(cu[b + 1])
     k = c1 - c0 - 1
     ok = (c0 >= 0 and c1 <= total_rows and 0 <= k <= max_k
           and c0 - b >= 0 and c0 - b + k <= total_rows - batch
-          and all(c0 >= int(cu[e]) for e in range(b)))
+          and all(c0 >= int(cu[e]) for e in range(b))
+          and all(c0 - b >= int(cu[e]) - e for e in range(b)))
     return k, ok
 
 

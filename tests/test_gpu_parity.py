@@ -324,6 +324,25 @@ def test_offsets_going_back():
     assert int(gpu["status"][2]) == oracle.ROW_BAD_K and int(gpu["status"][3]) == oracle.ROW_BAD_K
 
 
+def test_offsets_going_back_draft_logit_requests():
+    """Draft-logit requests with broken offsets (k = 5, so packed offsets are
+    0, 6, 12, ...): request 2 has negative length, request 3 starts below
+    request 2's offset, request 4's target rows follow every earlier offset
+    but its draft rows would reach into request 1's, request 6 is valid again
+    and request 7 is too long.  Every workgroup that reads a request's rows
+    must give the oracle's verdict (no hand-off word left in flight, no
+    time-out for request 6), and a clean call on the same workspace follows."""
+    w = synth.make(1, seed=3, batch=8, vocab=9000)
+    cu = w.cu_seqlens.copy()
+    cu[3], cu[4], cu[5], cu[6], cu[7] = 9, 13, 19, 26, 32
+    w.cu_seqlens = cu
+    gpu, counts = check(w)
+    st = [int(v) for v in gpu["status"]]
+    assert [s == oracle.ROW_BAD_K for s in st] == [False, False, True, True, True, True, False, True]
+    assert counts["status"] >= 5
+    check(synth.make(1, seed=4, batch=8, vocab=9000))
+
+
 def test_residual_paths_around_the_peer_limit():
     """Rows of 32 chunks (the helpers of a rejection exchange their residual
     masses and the chunk's holder draws) and of 33 chunks (one helper gathers

@@ -337,6 +337,43 @@ def test_status_codes():
     assert oracle.request_bounds(np.array([0, 2, 6]), 1, 2, 6, 8)[1]
 
 
+def test_request_bounds_never_overlap():
+    """The offsets rule keeps its promise: over random offsets, many of them
+    broken (requests with no rows, offsets that go back or jump), no two valid
+    requests share a target row or a draft row, every valid request's rows lie
+    inside the buffers, and correctly packed offsets are all valid."""
+    rng = np.random.default_rng(11)
+    for _ in range(3000):
+        B = int(rng.integers(1, 8))
+        max_k = 4
+        ks = rng.integers(-2, 6, size=B) if rng.random() < 0.7 else rng.integers(0, max_k + 1, size=B)
+        cu = np.concatenate([[0], np.cumsum(ks + 1)]).astype(np.int64)
+        packed = bool(np.all((ks >= 0) & (ks <= max_k)))
+        if rng.random() < 0.5:
+            cu[int(rng.integers(1, B + 1))] += int(rng.integers(-5, 6))
+            packed = False
+        total_rows = max(int(cu[-1]), B) + int(rng.integers(0, 3))
+        valid = []
+        for b in range(B):
+            k, ok = oracle.request_bounds(cu, b, B, total_rows, max_k)
+            if ok:
+                c0 = int(cu[b])
+                assert 0 <= c0 and c0 + k + 1 <= total_rows
+                assert 0 <= c0 - b and c0 - b + k <= total_rows - B
+                valid.append((set(range(c0, c0 + k + 1)), set(range(c0 - b, c0 - b + k))))
+        for i in range(len(valid)):
+            for j in range(i + 1, len(valid)):
+                assert not (valid[i][0] & valid[j][0]), cu
+                assert not (valid[i][1] & valid[j][1]), cu
+        if packed and int(cu[-1]) <= total_rows:
+            assert len(valid) == B, cu
+    # request 4's target rows follow every earlier offset, but its draft rows
+    # (9..13) would reach into request 1's (5..9)
+    cu = np.array([0, 6, 12, 9, 13, 19, 26, 32, 48])
+    assert [oracle.request_bounds(cu, b, 8, 48, 5)[1] for b in range(8)] == \
+        [True, True, False, False, False, False, True, False]
+
+
 def test_greedy_temperature_rule():
     assert oracle.is_greedy_temperature(0.0)
     assert oracle.is_greedy_temperature(-1.0)
