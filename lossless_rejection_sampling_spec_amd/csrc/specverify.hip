@@ -868,10 +868,12 @@ __device__ __forceinline__ void produce(const Params& P, const Req& R, int b, in
 }
 
 // Draft strip of request b, draft row j, strip s (draft-logit requests): the
-// statistics of S chunks of the draft row, two chunks in flight, published to
-// the draft hand-off words.  Draft strips come first in the grid, so the draft
-// rows stream while the target strips start, with the same bytes per
-// workgroup.
+// statistics of S chunks of the draft row, three chunks in flight (chunks t+1
+// and t+2 are requested before chunk t is reduced), published to the draft
+// hand-off words.  Draft strips come first in the grid, so the draft rows
+// stream while the target strips start, with the same bytes per workgroup;
+// with fewer workgroups streaming beside them than the producers have, a
+// deeper window pays here.
 template <typename TT, typename TD, bool AL>
 __device__ __forceinline__ void produce_draft(const Params& P, const Req& R, int b, int cu0, int j,
                                               int s, ProdShared& ps, Buf<TT, TD>& A) {
@@ -886,10 +888,11 @@ __device__ __forceinline__ void produce_draft(const Params& P, const Req& R, int
   constexpr int S = Strip<TT>::S;
   Buf<TT, TD> Q[S];
   Q[0] = A;
+  if (S > 1) issue_task<TT, TD, AL>((const TT*)nullptr, drow, true, c_begin + min(1, nt - 1), P.vocab, Q[1]);
 #pragma unroll
   for (int t = 0; t < S; ++t) {
-    if (t + 1 < S)
-      issue_task<TT, TD, AL>((const TT*)nullptr, drow, true, c_begin + min(t + 1, nt - 1), P.vocab, Q[t + 1]);
+    if (t + 2 < S)
+      issue_task<TT, TD, AL>((const TT*)nullptr, drow, true, c_begin + min(t + 2, nt - 1), P.vocab, Q[t + 2]);
     if (t < nt) produce_task<TD, TT, TD, AL>(P, R, Q[t], true, c_begin + t, -1, taud, t, ps);
   }
   __syncthreads();
