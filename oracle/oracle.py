@@ -494,8 +494,13 @@ def excusal(rec: SampledRecord, gpu_a: int, gpu_t: int, window: float = NEAR_TIE
     |u_i - theta_i| < window; a differing final token t' is excused iff u
     lies in the oracle's interval of t' widened by the window and t' has
     positive mass.  A request whose filters hit a top-p near tie is excused
-    whenever it differs.
+    whenever it differs.  An accepted count outside [0, k] or a token outside
+    the vocabulary always fails.
     """
+    k = len(rec.p_x)
+    if not (0 <= gpu_a <= k) or gpu_t < 0 or (rec.final_w is not None
+                                               and gpu_t >= len(rec.final_w)):
+        return "fail"          # outside the outputs any correct verify can give
     if gpu_a == rec.a and gpu_t == rec.t:
         return "match"
     if rec.near_tie:

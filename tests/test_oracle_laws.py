@@ -2,8 +2,9 @@
 distribution at V=8, k=2 (losslessness, the theorem stated on the Draft-Model
 -Sampling page, Key Topic 2, and on the Rust page, section "The Memory
 Bandwidth Wall and Speculative Math"), the acceptance law and its closed form
-(Key Topic 4), the one-hot invariant (FreeToken PR #836, Design: sampling
-each row and accepting the matching prefix is exact rejection sampling), the
+(Key Topic 4), the one-hot invariant (FreeToken PR #836, Design: with argmax
+drafts, drawing every verify row and keeping the prefix that agrees with the
+drafts has the law of rejection sampling), the
 greedy degenerate case (catalog page, Verification and sampling item 2) and
 the 0 % / 100 % acceptance edges (catalog page, Acceptance bars item 3).
 
