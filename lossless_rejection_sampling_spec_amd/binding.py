@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 
 SV_F32, SV_BF16 = 0, 1
 ONEHOT, LOGITS, PROBS = 0, 1, 2
-ROW_OK, ROW_NONFINITE, ROW_EMPTY, ROW_BAD_K, ROW_BAD_TOKEN, ROW_BAD_PARAM = range(6)
+ROW_OK, ROW_NONFINITE, ROW_EMPTY, ROW_BAD_K, ROW_BAD_TOKEN, ROW_BAD_PARAM, ROW_INTERNAL = range(7)
 MAX_K = 63
 
 _lib = None
@@ -112,14 +112,38 @@ def _check_vec(t: torch.Tensor | None, name: str, dtype, n: int | None = None) -
 
 
 def get_workspace(device: torch.device, nbytes: int) -> torch.Tensor:
-    """A zero-initialised workspace cached per device (the library leaves it
-    ready after every call, so it is reused without clearing)."""
-    key = (device.type, device.index)
+    """A zero-initialised workspace cached per (device, current stream).
+
+    The library leaves a workspace ready after every call, so it is reused
+    without clearing.  Calls that may run concurrently must not share one, so
+    each stream gets its own: calls on one stream are ordered by the stream."""
+    device = torch.device(device)
+    stream = torch.cuda.current_stream(device)
+    key = (device.type, device.index, stream.cuda_stream)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _ws_cache[key] = ws
     return ws
+
+
+def reset_workspace(workspace: torch.Tensor | None = None, device=None) -> None:
+    """Zero-fill a workspace on the current stream (spec_verify_workspace_init).
+
+    Call it after any request reports ROW_INTERNAL (a wait between the
+    library's workgroups ran out): such a call can leave hand-off words in
+    flight that the next call would take as fresh.  With no argument, every
+    workspace cached for `device` (default: the current device) is cleared,
+    each on the stream it belongs to."""
+    if workspace is not None:
+        targets = [(workspace, torch.cuda.current_stream(workspace.device).cuda_stream)]
+    else:
+        dev = torch.device(device) if device is not None else torch.device(
+            "cuda", torch.cuda.current_device())
+        targets = [(ws, key[2]) for key, ws in _ws_cache.items()
+                   if key[0] == dev.type and key[1] == dev.index]
+    for ws, stream in targets:
+        _raise(lib().spec_verify_workspace_init(_ptr(ws), ws.numel(), stream))
 
 
 def _raise(rc: int) -> None:

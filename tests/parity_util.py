@@ -17,6 +17,13 @@ import oracle
 REL = 1e-5
 ABS = 1e-30
 
+# comparison counts of every GPU check in this session, printed at its end
+SESSION_COUNTS: list = []
+
+
+def record_counts(label: str, counts: dict) -> None:
+    SESSION_COUNTS.append((label, dict(counts)))
+
 
 def run_oracle(w, greedy_entry=False, keep_cdf=True):
     return oracle.verify(w.target, w.target_dtype, w.cu_seqlens, w.draft_tokens,

@@ -11,7 +11,7 @@ torch = pytest.importorskip("torch")
 
 import oracle  # noqa: E402
 from lossless_rejection_sampling_spec_amd import binding, synth  # noqa: E402
-from parity_util import compare, run_oracle, sub_workload, to_numpy  # noqa: E402
+from parity_util import compare, record_counts, run_oracle, sub_workload, to_numpy  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -66,6 +66,7 @@ def check(w, requests=None, greedy_entry=False):
     ora = run_oracle(ref_w, greedy_entry=greedy_entry)
     counts = compare(w, gpu, ora, requests=requests, greedy_entry=greedy_entry)
     say(f"  {counts}")
+    record_counts(f"{w.name} seed={w.seed}", counts)
     return gpu, counts
 
 
@@ -104,16 +105,12 @@ def test_config1_full_size():
     check(synth.make(1))
 
 
-def test_config4_full_size_sampled_requests():
-    w = synth.make(4, batch=512)
-    reqs = list(range(0, 512, 8))
-    check(w, requests=reqs)
+def test_config4_full_size():
+    check(synth.make(4))
 
 
-def test_config3_full_size_sampled_requests():
-    w = synth.make(3)
-    reqs = list(range(0, 256, 8))
-    check(w, requests=reqs)
+def test_config3_full_size():
+    check(synth.make(3))
 
 
 # ------------------------------------------------------------------ greedy entry point
