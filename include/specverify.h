@@ -57,13 +57,18 @@
  *   SV_ROW_EMPTY     a needed logit row with no finite value
  *   SV_ROW_INTERNAL  see the enum below
  *   A request with a non-OK status gets accepted[b] = -1, out_tokens -1 and
- *   NaN probabilities; BAD_K requests leave out_tokens/probabilities untouched.
+ *   NaN probabilities; BAD_K requests leave out_tokens/probabilities untouched;
+ *   for SV_ROW_INTERNAL only status and accepted are defined.
+ *   Each output word of a request has one writer.
  * Workspace: device memory of at least spec_verify_workspace_bytes(); it must
  *   be zero-filled before its first use (spec_verify_workspace_init does it on
  *   a stream).  It is viewed as 64-bit words whose top bit marks a value in
- *   flight between workgroups; every call leaves that bit clear in every word,
- *   so the same workspace serves the next call whatever its sizes.  Two calls
- *   that may run concurrently must not share a workspace.
+ *   flight between workgroups; every call that reports no SV_ROW_INTERNAL
+ *   leaves that bit clear in every word, so the same workspace serves the next
+ *   call whatever its sizes.  A wait that runs out marks the workspace as
+ *   poisoned: from then on every call on it reports SV_ROW_INTERNAL for each
+ *   valid request until spec_verify_workspace_init clears it.  Two calls that
+ *   may run concurrently must not share a workspace.
  * Determinism: identical inputs give bitwise identical outputs, and request
  *   b's results do not depend on the other requests of the batch.
  */
@@ -111,8 +116,10 @@ enum {
   SV_ROW_BAD_TOKEN = 4,
   SV_ROW_BAD_PARAM = 5,
   SV_ROW_INTERNAL = 6   /* a wait between workgroups ran out (another kernel kept the
-                           GPU's compute units busy for a long time); the outputs of the
-                           request are -1 and the workspace should be re-initialised */
+                           GPU's compute units busy for a long time), or the workspace
+                           was poisoned by such a call: accepted is -1, the request's
+                           other outputs are undefined, and the workspace must be
+                           re-initialised (spec_verify_workspace_init) */
 };
 
 /* ABI version of the loaded library (SPECVERIFY_ABI_VERSION). */

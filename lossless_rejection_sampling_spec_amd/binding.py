@@ -36,34 +36,38 @@ class SpecVerifyError(RuntimeError):
     pass
 
 
+def load_library(path: str) -> ctypes.CDLL:
+    """Open a build of the library at `path` with the C ABI's signatures."""
+    if not os.path.exists(path):
+        raise SpecVerifyError(
+            f"{path} is missing; build it with `python -m lossless_rejection_sampling_spec_amd.build`")
+    L = ctypes.CDLL(path)
+    L.spec_verify_abi_version.restype = _i32
+    L.spec_verify_abi_version.argtypes = []
+    L.spec_verify_status_string.restype = ctypes.c_char_p
+    L.spec_verify_status_string.argtypes = [_i32]
+    L.spec_verify_workspace_bytes.restype = _sz
+    L.spec_verify_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
+    L.spec_verify_workspace_init.restype = _i32
+    L.spec_verify_workspace_init.argtypes = [_vp, _sz, _vp]
+    L.spec_verify_greedy.restype = _i32
+    L.spec_verify_greedy.argtypes = [
+        _vp, _i32, _i64, _vp, _vp, _i32, _i32, _i32, _i32,
+        _vp, _vp, _vp, _vp, _sz, _vp]
+    L.spec_verify_sampled.restype = _i32
+    L.spec_verify_sampled.argtypes = [
+        _vp, _i32, _i64, _vp, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+        _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+    return L
+
+
 def lib() -> ctypes.CDLL:
     """Load libspecverify.so (once).  Raises if it has not been built."""
     global _lib
     if _lib is None:
         with _lock:
             if _lib is None:
-                if not os.path.exists(LIB_PATH):
-                    raise SpecVerifyError(
-                        f"{LIB_PATH} is missing; build it with "
-                        "`python -m lossless_rejection_sampling_spec_amd.build`")
-                L = ctypes.CDLL(LIB_PATH)
-                L.spec_verify_abi_version.restype = _i32
-                L.spec_verify_abi_version.argtypes = []
-                L.spec_verify_status_string.restype = ctypes.c_char_p
-                L.spec_verify_status_string.argtypes = [_i32]
-                L.spec_verify_workspace_bytes.restype = _sz
-                L.spec_verify_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
-                L.spec_verify_workspace_init.restype = _i32
-                L.spec_verify_workspace_init.argtypes = [_vp, _sz, _vp]
-                L.spec_verify_greedy.restype = _i32
-                L.spec_verify_greedy.argtypes = [
-                    _vp, _i32, _i64, _vp, _vp, _i32, _i32, _i32, _i32,
-                    _vp, _vp, _vp, _vp, _sz, _vp]
-                L.spec_verify_sampled.restype = _i32
-                L.spec_verify_sampled.argtypes = [
-                    _vp, _i32, _i64, _vp, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                    _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
-                _lib = L
+                _lib = load_library(LIB_PATH)
     return _lib
 
 

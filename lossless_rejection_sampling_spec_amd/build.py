@@ -13,6 +13,10 @@ ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "specverify.hip")
 INC = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libspecverify.so")
+# Test-only build: every wait between workgroups gives up after one poll, so
+# the give-up path (SV_ROW_INTERNAL, the poisoned workspace) runs with every
+# kernel exiting normally.  Only the GPU tests load it.
+LIB_ONE_POLL = os.path.join(PKG, "libspecverify_onepoll.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -36,13 +40,22 @@ def hipcc() -> str:
     return cand
 
 
-def build(verbose: bool = True) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INC, "-o", tmp, SRC]
+def _start(out: str, extra: list, verbose: bool):
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", INC, "-o", out + ".tmp", SRC]
     if verbose:
         print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    return subprocess.Popen(cmd)
+
+
+def build(verbose: bool = True) -> str:
+    """Compile the library and its one-poll test build, side by side (every call)."""
+    jobs = [(LIB, _start(LIB, [], verbose)),
+            (LIB_ONE_POLL, _start(LIB_ONE_POLL, ["-DSV_SPIN_MAX=1"], verbose))]
+    failed = [out for out, proc in jobs if proc.wait() != 0]
+    if failed:
+        raise RuntimeError(f"hipcc failed for {failed}")
+    for out, _ in jobs:
+        os.replace(out + ".tmp", out)
     return LIB
 
 

@@ -80,7 +80,10 @@ constexpr int EPT = CHUNK / WG;   // elements per thread per chunk
 constexpr int MAX_NC = 512;       // chunks per row (vocab <= 4,194,304)
 constexpr int MAX_K = 63;         // k+1 positions fit one wave
 constexpr int STAGE_MAX = 49152;  // bytes of LDS the finalizer may stage statistics in
-constexpr int SPIN_MAX = 1 << 18; // polls before a wait gives up
+#ifndef SV_SPIN_MAX
+#define SV_SPIN_MAX (1 << 18)
+#endif
+constexpr int SPIN_MAX = SV_SPIN_MAX;  // polls before a wait gives up
 constexpr float NEG_INF = -__builtin_inff();
 constexpr float POS_INF = __builtin_inff();
 constexpr double LOG2E = 1.4426950408889634;
@@ -131,6 +134,8 @@ struct Params {
   u64* res;       // [batch][nc][nc] residual masses sent between helpers ([batch][nc] for nc > PEER_MAX)
   u64* thr_t;     // NULL when no request filters; float bits in the low half
   u64* thr_d;
+  u64* pq;        // [batch][2 * max_k] p(x_i), q(x_i) handed to the last helper of a request
+  u64* ctl;       // [0]: nonzero once a wait ran out (the workspace is poisoned)
   int64_t ld_t, ld_d;
   int batch, total_rows, max_k, vocab, nc;
   int S;          // chunks per producer strip
@@ -330,6 +335,11 @@ __device__ __forceinline__ u64 take_w(u64* w) {
   }
   return 0ull;
 }
+
+// A wait that ran out leaves hand-off words in flight that a later call would
+// take as fresh: the workspace is marked, and every call on it reports
+// SV_ROW_INTERNAL until spec_verify_workspace_init clears the mark.
+__device__ __forceinline__ void poison(u64* ctl) { st_agent(ctl, 1ull); }
 
 
 // ---------------------------------------------------------------------------
@@ -1121,6 +1131,7 @@ struct FinShared {
   float lx[64], sx[64], dlx[64];
   int x[64];
   float u[64];   // the request's uniforms, read with the draft ids
+  float px[64], qx[64];   // p(x_j), q(x_j) handed to the last helper (mode 2)
   int a, code, mode, timeout;
 };
 
@@ -1137,7 +1148,9 @@ __device__ __forceinline__ void finalize(const Params& P, int b, int cu0, int k,
   float* st_m = reinterpret_cast<float*>(stage);
   uint32_t* st_s = stage + (size_t)(2 * P.max_k + 1) * nc;
 
-  if (tid == 0) fs.timeout = 0;
+  // a poisoned workspace may hold stale hand-off words: take none of them
+  const bool poisoned = ldu(P.ctl) != 0ull;
+  if (tid == 0) fs.timeout = poisoned ? 1 : 0;
   if (tid < 64) {
     fs.x[tid] = (tid < k) ? P.drafts[d0 + tid] : -1;
     // uniforms exist for sampled requests only (the greedy entry passes none)
@@ -1147,7 +1160,7 @@ __device__ __forceinline__ void finalize(const Params& P, int b, int cu0, int k,
   bool badtok_any = false;
   for (int i = 0; i < k; ++i) badtok_any |= (fs.x[i] < 0 || fs.x[i] >= P.vocab);
 
-  if (!R.bad_param) {
+  if (!R.bad_param && !poisoned) {
     // wait for, stage and consume every word the request's producers published
     // (also when a draft id is out of range: the statistics were still written)
     const int nA = (k + 1) * nc;
@@ -1190,7 +1203,10 @@ __device__ __forceinline__ void finalize(const Params& P, int b, int cu0, int k,
         fs.dlx[jr] = __uint_as_float(pay);
       }
     }
-    if (to) atomicOr(&fs.timeout, 1);
+    if (to) {
+      atomicOr(&fs.timeout, 1);
+      poison(P.ctl);
+    }
   }
   __syncthreads();
 
@@ -1304,7 +1320,14 @@ __device__ __forceinline__ void finalize(const Params& P, int b, int cu0, int k,
     int a = (int)__builtin_ctzll(~m_acc);
     if (a > k) a = k;
     fs.M[j] = M; fs.Mq[j] = Mq; fs.S[j] = S; fs.Sq[j] = Sq;
-    if (code == SV_ROW_OK) {
+    // mode 2 (a rejection under a logit or probability draft): the helpers
+    // finish the request, and its last helper is the only writer of its outputs
+    const bool resid = code == SV_ROW_OK && sampled && a < k && R.kind != SV_DRAFT_ONEHOT;
+    if (resid && j < k) {
+      fs.px[j] = (float)px;
+      fs.qx[j] = (float)qx;
+    }
+    if (code == SV_ROW_OK && !resid) {
       if (j < k) {
         if (P.p_at) P.p_at[d0 + j] = (float)px;
         if (P.q_at) P.q_at[d0 + j] = (float)qx;
@@ -1331,6 +1354,7 @@ __device__ __forceinline__ void finalize(const Params& P, int b, int cu0, int k,
   const int mode = fs.mode;
   if (code != SV_ROW_OK) {
     write_fault(P, b, cu0, k, code);
+    // the helpers take a record even on a poisoned workspace, so they never wait long
     if (has_helpers(P, R)) helpers_none(P, b);
     return;
   }
@@ -1354,7 +1378,24 @@ __device__ __forceinline__ void finalize(const Params& P, int b, int cu0, int k,
     if (tid == 0) P.out[row] = t;
     if (has_helpers(P, R)) helpers_none(P, b);
   } else if (mode == 2) {
+    // "pending" until the last helper writes the request's outputs: if no helper
+    // completes them (a wait ran out) the caller still sees INTERNAL.  Both
+    // stores write through to memory, and the wave waits for them before the
+    // records are posted, so the helper's stores, made after it takes a record,
+    // land later.
+    if (tid == 0) {
+      st_agent(P.status + b, (int32_t)SV_ROW_INTERNAL);
+      st_agent(P.accepted + b, (int32_t)-1);
+      // both stores completed (the compiler's own wait insertion drops an
+      // explicit wait that no later instruction of this wave depends on)
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
     // every word of every record carries its own tag: no ordering among them
+    if (tid < 2 * k) {
+      const float v = tid < k ? fs.px[tid] : fs.qx[tid - k];
+      put_w(P.pq + (int64_t)b * 2 * P.max_k + tid, 0u, __float_as_uint(v));
+    }
     const u64 sp = (u64)__double_as_longlong(fs.S[a]);
     const u64 sq = (u64)__double_as_longlong(fs.Sq[a]);
     for (int e = tid; e < nc * DEC_W; e += WG) {
@@ -1374,7 +1415,7 @@ __device__ __forceinline__ void finalize(const Params& P, int b, int cu0, int k,
       put_w(P.dec + (int64_t)b * nc * DEC_W + e, f == 0 ? (uint32_t)a : 0u, pay);
     }
   }
-  if (tid == 0) {
+  if (tid == 0 && mode != 2) {
     P.accepted[b] = a;
     P.status[b] = SV_ROW_OK;
   }
@@ -1425,8 +1466,30 @@ __device__ __forceinline__ void res_ctx(const Params& P, const Req& R, const Set
 
 struct HelpShared {
   u64 rec[DEC_W];
+  float pq[2 * 64];   // the last helper's copy of p(x_j), q(x_j)
   int timeout, bad;
 };
+
+// The outputs of a request that rejected under a logit or probability draft,
+// written by its last helper alone (the drawing helper writes the token at the
+// stop position): accepted drafts, -1 past the stop position, p and q at the
+// drafts, the accepted count and the status.
+__device__ __forceinline__ void finish_outputs(const Params& P, int b, int cu0, int k, int a,
+                                               const HelpShared& hs) {
+  const int d0 = cu0 - b;
+  for (int j = threadIdx.x; j <= k; j += WG) {
+    if (j < a) P.out[cu0 + j] = P.drafts[d0 + j];
+    else if (j > a) P.out[cu0 + j] = -1;
+  }
+  for (int j = threadIdx.x; j < k; j += WG) {
+    if (P.p_at) P.p_at[d0 + j] = hs.pq[j];
+    if (P.q_at) P.q_at[d0 + j] = hs.pq[k + j];
+  }
+  if (threadIdx.x == 0) {
+    st_agent(P.accepted + b, (int32_t)a);
+    st_agent(P.status + b, (int32_t)SV_ROW_OK);
+  }
+}
 
 template <typename TT, typename TD, bool AL>
 __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, int c, Smem& sm,
@@ -1444,11 +1507,28 @@ __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, i
 #pragma unroll
     for (int f = 0; f < DEC_W; ++f) to = to || !(hi32(hs.rec[f]) & TAG);
     if (to) {
-      if (last) write_fault(P, b, cu0, k, SV_ROW_INTERNAL);
+      // the finalizer's outputs (or its pending INTERNAL) stand: nothing is written here
+      if (threadIdx.x == 0) poison(P.ctl);
       return;
     }
   }
   if (hi32(hs.rec[0]) & F_NONE) return;
+  if (last) {
+    // p(x_j) and q(x_j) of the request, for the outputs this helper writes
+    if (threadIdx.x == 0) hs.timeout = 0;
+    __syncthreads();
+    if (threadIdx.x < 2 * k) {
+      const u64 v = take_w(P.pq + (int64_t)b * 2 * P.max_k + threadIdx.x);
+      if (!(hi32(v) & TAG)) atomicOr(&hs.timeout, 1);
+      hs.pq[threadIdx.x] = __uint_as_float(lo32(v));
+    }
+    __syncthreads();
+    if (hs.timeout) {
+      if (threadIdx.x == 0) poison(P.ctl);
+      write_fault(P, b, cu0, k, SV_ROW_INTERNAL);
+      return;
+    }
+  }
   Setup su;
   su.Sp = __longlong_as_double((long long)((u64)lo32(hs.rec[2]) | ((u64)lo32(hs.rec[3]) << 32)));
   su.Sq = __longlong_as_double((long long)((u64)lo32(hs.rec[4]) | ((u64)lo32(hs.rec[5]) << 32)));
@@ -1459,6 +1539,7 @@ __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, i
   const float cmq = logits ? __uint_as_float(lo32(hs.rec[1])) : 0.f;
   const int a = su.a;
   if (a < 0 || a >= k) {   // cannot happen after a fresh decision; never index with it
+    if (threadIdx.x == 0) poison(P.ctl);
     if (last) write_fault(P, b, cu0, k, SV_ROW_INTERNAL);
     return;
   }
@@ -1531,13 +1612,17 @@ __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, i
       if (hi32(v) & F_BAD) bd = 1;
       ds.E[t] = (double)__uint_as_float(lo32(v));
     }
-    if (to) atomicOr(&hs.timeout, 1);
+    if (to) {
+      atomicOr(&hs.timeout, 1);
+      poison(P.ctl);
+    }
     if (bd) atomicOr(&hs.bad, 1);
     __syncthreads();
     if (hs.timeout || hs.bad) {
       if (last) write_fault(P, b, cu0, k, hs.timeout ? SV_ROW_INTERNAL : SV_ROW_NONFINITE);
       return;
     }
+    if (last) finish_outputs(P, b, cu0, k, a, hs);
     if (!pick_chunk(nc, u, ds)) {
       if (last) {
         const float tau = (P.thr_t && R.filt) ? thr_of(P.thr_t, trow) : NEG_INF;
@@ -1585,14 +1670,21 @@ __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, i
     ds.E[cc] = (double)__uint_as_float(lo32(v));
   }
   if (threadIdx.x == 0) ds.E[nc - 1] = (double)(float)W;
-  if (to) atomicOr(&hs.timeout, 1);
+  if (to) {
+    atomicOr(&hs.timeout, 1);
+    poison(P.ctl);
+  }
   if (bd) atomicOr(&hs.bad, 1);
   __syncthreads();
   if (hs.timeout) {
     write_fault(P, b, cu0, k, SV_ROW_INTERNAL);
+    return;
   } else if (hs.bad) {
     write_fault(P, b, cu0, k, SV_ROW_NONFINITE);
-  } else if (!pick_chunk(nc, u, ds)) {
+    return;
+  }
+  finish_outputs(P, b, cu0, k, a, hs);
+  if (!pick_chunk(nc, u, ds)) {
     // residual mass is exactly zero: draw from p of the rejected row, using the
     // row's chunk statistics (their payloads stay in the words after consumption)
     const float tau = (P.thr_t && R.filt) ? thr_of(P.thr_t, trow) : NEG_INF;
@@ -2020,7 +2112,7 @@ __global__ void k_fill_zero(uint4* p, size_t n16, unsigned char* tail, size_t nt
 // host side
 // ---------------------------------------------------------------------------
 struct Layout {
-  size_t cst, dst, rx, dec, res, thr_t, thr_d, total;
+  size_t cst, dst, rx, dec, res, thr_t, thr_d, pq, ctl, total;
 };
 
 static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -2033,6 +2125,9 @@ static bool layout(int batch, int total_rows, int vocab, int max_k, Layout& L, i
   const size_t B = (size_t)batch, R = (size_t)total_rows, D = (size_t)(total_rows - batch);
   const size_t D1 = D ? D : 1;
   size_t o = 0;
+  // the control words sit at a fixed place whatever the sizes: a workspace
+  // serves calls of any size, and the other regions move with them
+  L.ctl = o; o = align_up(o + 32 * sizeof(u64));
   L.cst = o; o = align_up(o + R * nc * sizeof(u64));
   L.dst = o; o = align_up(o + D1 * nc * sizeof(u64));
   L.rx = o; o = align_up(o + R * 3 * sizeof(u64));
@@ -2040,6 +2135,7 @@ static bool layout(int batch, int total_rows, int vocab, int max_k, Layout& L, i
   L.res = o; o = align_up(o + B * nc * (nc <= PEER_MAX ? nc : 1) * sizeof(u64));
   L.thr_t = o; o = align_up(o + R * sizeof(u64));
   L.thr_d = o; o = align_up(o + D1 * sizeof(u64));
+  L.pq = o; o = align_up(o + B * (size_t)(2 * max_k + 1) * sizeof(u64));
   L.total = o;
   return true;
 }
@@ -2118,6 +2214,8 @@ static void carve(Params& P, void* ws, const Layout& L) {
   P.res = (u64*)(w + L.res);
   P.thr_t = (u64*)(w + L.thr_t);
   P.thr_d = (u64*)(w + L.thr_d);
+  P.pq = (u64*)(w + L.pq);
+  P.ctl = (u64*)(w + L.ctl);
 }
 
 }  // namespace sv
