@@ -94,7 +94,9 @@ enum {
                            would be too large */
   SV_ERR_DTYPE = 3,     /* unknown dtype code */
   SV_ERR_WORKSPACE = 4, /* workspace_bytes smaller than required */
-  SV_ERR_LAUNCH = 5     /* the HIP runtime refused a launch */
+  SV_ERR_LAUNCH = 5,    /* the HIP runtime refused a launch */
+  SV_ERR_SCRATCH = 6    /* spec_verify_sampled_noalloc: the call needs more than its
+                           static scratch array holds (8 MiB) */
 };
 
 /* element types of logit / probability buffers */
@@ -193,6 +195,33 @@ int spec_verify_sampled(const void* target_logits, int target_dtype, int64_t ld_
                         int32_t* accepted, int32_t* out_tokens,
                         float* p_at_draft, float* q_at_draft, int32_t* status,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spec_verify_sampled without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It calls no hipMalloc, hipFree or other
+ * allocating routine: its scratch is one static device array of 8 MiB per GPU
+ * (held until the process ends; its address is looked up once per device).
+ * Each call zero-fills the bytes it uses with a small kernel on `stream`, then
+ * runs the same kernels as spec_verify_sampled, with the same results.
+ *   Arguments, layouts and outputs: as spec_verify_sampled.
+ *   Returns SV_ERR_SCRATCH (nothing enqueued) when
+ *   spec_verify_workspace_bytes(batch, total_rows, vocab, max_k) > 8 MiB
+ *   (B=512, k=5, V=152064 needs 3.1 MB), and SV_ERR_LAUNCH when the array's
+ *   address cannot be found on the current device.
+ *   Every call on one GPU uses that GPU's one array: two calls that may
+ *   overlap on the same GPU (concurrent streams, threads) race and must not
+ *   be issued.
+ */
+int spec_verify_sampled_noalloc(const void* target_logits, int target_dtype, int64_t ld_target,
+                                const void* draft, int draft_dtype, int64_t ld_draft,
+                                const int32_t* draft_kind, const int32_t* cu_seqlens,
+                                const int32_t* draft_tokens, const float* uniforms,
+                                const float* temperature, const int32_t* top_k,
+                                const float* top_p, int batch, int total_rows, int max_k,
+                                int vocab, int32_t* accepted, int32_t* out_tokens,
+                                float* p_at_draft, float* q_at_draft, int32_t* status,
+                                void* stream);
 
 #ifdef __cplusplus
 }

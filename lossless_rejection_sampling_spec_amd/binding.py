@@ -58,6 +58,10 @@ def load_library(path: str) -> ctypes.CDLL:
     L.spec_verify_sampled.argtypes = [
         _vp, _i32, _i64, _vp, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
         _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+    L.spec_verify_sampled_noalloc.restype = _i32
+    L.spec_verify_sampled_noalloc.argtypes = [
+        _vp, _i32, _i64, _vp, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+        _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]
     return L
 
 
@@ -229,6 +233,32 @@ def verify_sampled(target: torch.Tensor, draft: torch.Tensor | None, draft_kind:
         _ptr(uniforms), _ptr(temperature), _ptr(top_k), _ptr(top_p),
         batch, total_rows, max_k, V, _ptr(accepted), _ptr(tokens), _ptr(p_at), _ptr(q_at),
         _ptr(status), _ptr(ws), ws.numel(), _stream(dev))
+    _raise(rc)
+    return accepted, tokens, status, p_at, q_at
+
+
+def verify_sampled_noalloc(target: torch.Tensor, draft: torch.Tensor | None,
+                           draft_kind: torch.Tensor, cu_seqlens: torch.Tensor,
+                           draft_tokens: torch.Tensor, uniforms: torch.Tensor,
+                           temperature: torch.Tensor, top_k: torch.Tensor | None = None,
+                           top_p: torch.Tensor | None = None, *, max_k: int, vocab: int,
+                           out: tuple):
+    """spec_verify_sampled_noalloc: the sampled verify with the library's
+    static scratch array instead of a workspace.  `out` = (accepted, tokens,
+    status, p_at or None, q_at or None), preallocated by the caller, so this
+    call allocates nothing."""
+    batch = cu_seqlens.numel() - 1
+    total_rows = target.shape[0]
+    accepted, tokens, status, p_at, q_at = out
+    rc = lib().spec_verify_sampled_noalloc(
+        _ptr(target), _dtype_code(target), target.stride(0),
+        _ptr(draft), _dtype_code(draft) if draft is not None else SV_F32,
+        draft.stride(0) if draft is not None else 0,
+        _ptr(draft_kind), _ptr(cu_seqlens),
+        _ptr(draft_tokens) if total_rows > batch else None,
+        _ptr(uniforms), _ptr(temperature), _ptr(top_k), _ptr(top_p),
+        batch, total_rows, max_k, int(vocab), _ptr(accepted), _ptr(tokens), _ptr(p_at),
+        _ptr(q_at), _ptr(status), _stream(target.device))
     _raise(rc)
     return accepted, tokens, status, p_at, q_at
 

@@ -68,6 +68,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "specverify.h"
 
@@ -2218,6 +2219,109 @@ static void carve(Params& P, void* ws, const Layout& L) {
   P.ctl = (u64*)(w + L.ctl);
 }
 
+
+// ---------------------------------------------------------------------------
+// the scratch array of the allocation-free entry point
+// ---------------------------------------------------------------------------
+// One array per GPU, zero-filled by the loader and again, over the bytes a
+// call uses, by every call before its verify kernel.  In host code `scratch`
+// names a host-side stand-in: the device address comes from
+// hipGetSymbolAddress, once per device, and only that address is passed on.
+constexpr size_t SCRATCH_BYTES = (size_t)8 << 20;
+static __device__ __align__(256) unsigned char scratch[SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[MAX_DEVICES];
+
+// Device address of the current device's scratch array, or nullptr.
+static void* scratch_of_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+static int fill_zero(void* p, size_t nbytes, hipStream_t st) {
+  const size_t n16 = nbytes / 16;
+  const size_t ntail = nbytes - n16 * 16;
+  unsigned blocks = (unsigned)((n16 + 255) / 256);
+  if (blocks > 4096) blocks = 4096;
+  if (blocks == 0) blocks = 1;
+  hipLaunchKernelGGL(k_fill_zero, dim3(blocks), dim3(256), 0, st, (uint4*)p, n16,
+                     (unsigned char*)p + n16 * 16, ntail);
+  return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+}
+
+// The sampled verify with a caller's workspace, or (noalloc) with the
+// current device's scratch array, cleared first over the bytes it needs.
+static int sampled_call(const void* target_logits, int target_dtype, int64_t ld_target,
+                        const void* draft, int draft_dtype, int64_t ld_draft,
+                        const int32_t* draft_kind, const int32_t* cu_seqlens,
+                        const int32_t* draft_tokens, const float* uniforms,
+                        const float* temperature, const int32_t* top_k, const float* top_p,
+                        int batch, int total_rows, int max_k, int vocab, int32_t* accepted,
+                        int32_t* out_tokens, float* p_at_draft, float* q_at_draft,
+                        int32_t* status, void* workspace, size_t workspace_bytes, bool noalloc,
+                        void* stream) {
+  if (!target_logits || !draft_kind || !cu_seqlens || !uniforms || !temperature || !accepted ||
+      !out_tokens || !status)
+    return SV_ERR_NULL;
+  if (!draft_tokens && total_rows > batch) return SV_ERR_NULL;
+  if (target_dtype != SV_F32 && target_dtype != SV_BF16) return SV_ERR_DTYPE;
+  if (draft && draft_dtype != SV_F32 && draft_dtype != SV_BF16) return SV_ERR_DTYPE;
+  Layout L;
+  int nc;
+  if (!layout(batch, total_rows, vocab, max_k, L, nc) || ld_target < vocab ||
+      (draft && ld_draft < vocab) || !grid_ok(batch, max_k, nc))
+    return SV_ERR_SHAPE;
+  if (noalloc) {
+    if (L.total > SCRATCH_BYTES) return SV_ERR_SCRATCH;
+    workspace = scratch_of_current_device();
+    if (workspace == nullptr) return SV_ERR_LAUNCH;
+    workspace_bytes = SCRATCH_BYTES;
+    const int rc = fill_zero(workspace, L.total, (hipStream_t)stream);
+    if (rc != SV_OK) return rc;
+  }
+  if (workspace_bytes < L.total) return SV_ERR_WORKSPACE;
+  Params P = {};
+  P.target = target_logits;
+  P.draft = draft;
+  P.kind = draft_kind;
+  P.cu = cu_seqlens;
+  P.drafts = draft_tokens;
+  P.u = uniforms;
+  P.temp = temperature;
+  P.top_k = top_k;
+  P.top_p = top_p;
+  P.accepted = accepted;
+  P.out = out_tokens;
+  P.p_at = p_at_draft;
+  P.q_at = q_at_draft;
+  P.status = status;
+  P.ld_t = ld_target;
+  P.ld_d = draft ? ld_draft : 0;
+  P.batch = batch;
+  P.total_rows = total_rows;
+  P.max_k = max_k;
+  P.vocab = vocab;
+  P.nc = nc;
+  P.greedy_entry = 0;
+  carve(P, workspace, L);
+  const bool filters = top_k != nullptr || top_p != nullptr;
+  if (!filters) {
+    P.thr_t = nullptr;
+    P.thr_d = nullptr;
+  }
+  const int ddt = draft ? draft_dtype : target_dtype;
+  return dispatch(P, target_dtype, ddt, true, filters, (hipStream_t)stream);
+}
+
 }  // namespace sv
 
 using namespace sv;
@@ -2234,6 +2338,7 @@ const char* spec_verify_status_string(int code) {
     case SV_ERR_DTYPE: return "unknown dtype code";
     case SV_ERR_WORKSPACE: return "workspace smaller than spec_verify_workspace_bytes()";
     case SV_ERR_LAUNCH: return "kernel launch failed";
+    case SV_ERR_SCRATCH: return "the call needs more than the static scratch array holds";
     case 100 + SV_ROW_OK: return "row ok";
     case 100 + SV_ROW_NONFINITE: return "row: NaN/inf logit or invalid probability";
     case 100 + SV_ROW_EMPTY: return "row: no finite logit";
@@ -2255,14 +2360,7 @@ size_t spec_verify_workspace_bytes(int batch, int total_rows, int vocab, int max
 int spec_verify_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
   if (!workspace) return SV_ERR_NULL;
   if (workspace_bytes == 0) return SV_OK;
-  const size_t n16 = workspace_bytes / 16;
-  const size_t ntail = workspace_bytes - n16 * 16;
-  unsigned blocks = (unsigned)((n16 + 255) / 256);
-  if (blocks > 4096) blocks = 4096;
-  if (blocks == 0) blocks = 1;
-  hipLaunchKernelGGL(k_fill_zero, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
-                     (uint4*)workspace, n16, (unsigned char*)workspace + n16 * 16, ntail);
-  return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+  return fill_zero(workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 int spec_verify_greedy(const void* target_logits, int target_dtype, int64_t ld_target,
@@ -2310,49 +2408,26 @@ int spec_verify_sampled(const void* target_logits, int target_dtype, int64_t ld_
                         int32_t* out_tokens, float* p_at_draft, float* q_at_draft,
                         int32_t* status, void* workspace, size_t workspace_bytes,
                         void* stream) {
-  if (!target_logits || !draft_kind || !cu_seqlens || !uniforms || !temperature || !accepted ||
-      !out_tokens || !status || !workspace)
-    return SV_ERR_NULL;
-  if (!draft_tokens && total_rows > batch) return SV_ERR_NULL;
-  if (target_dtype != SV_F32 && target_dtype != SV_BF16) return SV_ERR_DTYPE;
-  if (draft && draft_dtype != SV_F32 && draft_dtype != SV_BF16) return SV_ERR_DTYPE;
-  Layout L;
-  int nc;
-  if (!layout(batch, total_rows, vocab, max_k, L, nc) || ld_target < vocab ||
-      (draft && ld_draft < vocab) || !grid_ok(batch, max_k, nc))
-    return SV_ERR_SHAPE;
-  if (workspace_bytes < L.total) return SV_ERR_WORKSPACE;
-  Params P = {};
-  P.target = target_logits;
-  P.draft = draft;
-  P.kind = draft_kind;
-  P.cu = cu_seqlens;
-  P.drafts = draft_tokens;
-  P.u = uniforms;
-  P.temp = temperature;
-  P.top_k = top_k;
-  P.top_p = top_p;
-  P.accepted = accepted;
-  P.out = out_tokens;
-  P.p_at = p_at_draft;
-  P.q_at = q_at_draft;
-  P.status = status;
-  P.ld_t = ld_target;
-  P.ld_d = draft ? ld_draft : 0;
-  P.batch = batch;
-  P.total_rows = total_rows;
-  P.max_k = max_k;
-  P.vocab = vocab;
-  P.nc = nc;
-  P.greedy_entry = 0;
-  carve(P, workspace, L);
-  const bool filters = top_k != nullptr || top_p != nullptr;
-  if (!filters) {
-    P.thr_t = nullptr;
-    P.thr_d = nullptr;
-  }
-  const int ddt = draft ? draft_dtype : target_dtype;
-  return dispatch(P, target_dtype, ddt, true, filters, (hipStream_t)stream);
+  if (!workspace) return SV_ERR_NULL;
+  return sampled_call(target_logits, target_dtype, ld_target, draft, draft_dtype, ld_draft,
+                      draft_kind, cu_seqlens, draft_tokens, uniforms, temperature, top_k, top_p,
+                      batch, total_rows, max_k, vocab, accepted, out_tokens, p_at_draft,
+                      q_at_draft, status, workspace, workspace_bytes, false, stream);
+}
+
+int spec_verify_sampled_noalloc(const void* target_logits, int target_dtype, int64_t ld_target,
+                                const void* draft, int draft_dtype, int64_t ld_draft,
+                                const int32_t* draft_kind, const int32_t* cu_seqlens,
+                                const int32_t* draft_tokens, const float* uniforms,
+                                const float* temperature, const int32_t* top_k,
+                                const float* top_p, int batch, int total_rows, int max_k,
+                                int vocab, int32_t* accepted, int32_t* out_tokens,
+                                float* p_at_draft, float* q_at_draft, int32_t* status,
+                                void* stream) {
+  return sampled_call(target_logits, target_dtype, ld_target, draft, draft_dtype, ld_draft,
+                      draft_kind, cu_seqlens, draft_tokens, uniforms, temperature, top_k, top_p,
+                      batch, total_rows, max_k, vocab, accepted, out_tokens, p_at_draft,
+                      q_at_draft, status, nullptr, 0, true, stream);
 }
 
 }  // extern "C"

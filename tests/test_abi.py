@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_strings():
     assert binding.abi_version() == 1
-    for code in range(6):
+    for code in range(7):
         assert binding.status_string(code)
     for code in range(6):
         assert binding.status_string(100 + code).startswith("row")
@@ -104,6 +104,18 @@ def test_greedy_validation():
     assert _greedy(wsb=0) == 4
 
 
+def test_noalloc_rejects_before_any_device_call():
+    fake = FAKE
+    L = binding.lib()
+    # a workspace far beyond the static scratch array: rejected on the host
+    assert L.spec_verify_sampled_noalloc(fake, 1, 1000000, None, 0, 0, fake, fake, fake, fake,
+                                         fake, None, None, 1024, 8192, 7, 1000000, fake, fake,
+                                         None, None, fake, None) == 6
+    assert L.spec_verify_sampled_noalloc(None, 1, 100, None, 0, 0, fake, fake, fake, fake, fake,
+                                         None, None, 2, 6, 3, 100, fake, fake, None, None, fake,
+                                         None) == 1
+
+
 def test_workspace_init_null():
     assert binding.lib().spec_verify_workspace_init(None, 100, None) == 1
 
@@ -117,7 +129,7 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
 
 def test_ctypes_signatures_match_header_arity():
     src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
-    for name in ("spec_verify_greedy", "spec_verify_sampled"):
+    for name in ("spec_verify_greedy", "spec_verify_sampled", "spec_verify_sampled_noalloc"):
         m = re.search(name + r"\s*\(([^;]*)\);", src, flags=re.S)
         n_args = len([a for a in m.group(1).split(",") if a.strip()])
         assert len(getattr(binding.lib(), name).argtypes) == n_args, name
