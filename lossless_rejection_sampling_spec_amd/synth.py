@@ -16,8 +16,8 @@ Recipe (all streams are numpy PCG64 keyed by SeedSequence(entropy, spawn_key=
 * draft logits   D = L_stored + sigma N(0,1), rounded to storage;
 * draft tokens   LOGITS: Gumbel-max over D/T restricted to the request's
   top-k set (temperature and top-k; the drafter does not apply top-p);
-  PROBS: Gumbel-max over log q; greedy and ONEHOT: lowest-index argmax of
-  L_stored + sigma N (a noisy copy that is not handed to the verifier);
+  PROBS: Gumbel-max over log q; greedy, ONEHOT and MATCH: lowest-index argmax
+  of L_stored + sigma N (a noisy copy that is not handed to the verifier);
 * uniforms       randint(0, 2^24) * 2^-24 as float32, k_b + 1 per request.
 """
 
@@ -28,7 +28,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 F32, BF16 = 0, 1
-ONEHOT, LOGITS, PROBS = 0, 1, 2
+ONEHOT, LOGITS, PROBS, MATCH = 0, 1, 2, 3
 DRAFT_SALT = 1 << 30
 
 # stream ids
@@ -177,7 +177,7 @@ def build(config: int, *, seed: int = 0, batch: int, vocab: int, ks, target_dtyp
         target[c0:c0 + k + 1, :vocab] = rows
         L = stored_f64(rows, target_dtype)
         T = float(temps[b])
-        if greedy[b] or kinds[b] == ONEHOT:
+        if greedy[b] or kinds[b] in (ONEHOT, MATCH):
             for i in range(k):
                 noisy = L[i] + sig[b] * rng_gn.standard_normal(vocab)
                 draft_tokens[d0 + i] = int(np.argmax(noisy))

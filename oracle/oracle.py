@@ -28,6 +28,12 @@ What it computes, and where the pages fix it
   first mismatch), the degenerate case of the above with a one-hot target:
   catalog page, sections "The existing base" and "Verification and
   sampling" item 2.
+* Prefix-match verify of argmax drafts (draft kind MATCH): every verify row
+  is sampled the way decode samples it, and the drafts are accepted while
+  each equals its row's sample; the sample at the first mismatch (or of the
+  last row) is committed.  Page "FreeToken PR #836", section "Design",
+  rejection row and the bullet on argmax drafts (the PR's own verify, equal
+  in law to rejection sampling with one-hot drafts).
 
 Readings where the pages are silent or disagree (each one is listed in
 DESIGN.md as well):
@@ -70,7 +76,7 @@ import numpy as np
 # dtype codes of the boundary
 F32, BF16 = 0, 1
 # draft kinds
-ONEHOT, LOGITS, PROBS = 0, 1, 2
+ONEHOT, LOGITS, PROBS, MATCH = 0, 1, 2, 3
 # per-request status codes
 ROW_OK, ROW_NONFINITE, ROW_EMPTY, ROW_BAD_K, ROW_BAD_TOKEN = 0, 1, 2, 3, 4
 
@@ -254,6 +260,38 @@ def final_draw(p_a, q_a, rejected: bool, u_final: float):
     return t, w, C, W, min(u_final - lo, hi - u_final), fb
 
 
+def match_request(p_rows, drafts, u) -> SampledRecord:
+    """Prefix-match verify of argmax drafts: y_j = inverse_cdf(p_j, u_j) for
+    every row j (each row's own uniform), a = the first j < k with y_j != x_j
+    (k if none), committed tokens x_0..x_{a-1}, y_a.
+
+    The record uses the fields of a sampled record: margins[j] is the distance
+    of u_j from the nearest end of x_j's interval [C_{x-1}/W, C_x/W) (the
+    boundary that decides the match), the final fields describe row a's draw.
+    p_x are p_j(x_j); q_x are 1 (a one-hot draft)."""
+    k = len(drafts)
+    xs = [int(d) for d in drafts]
+    margins = []
+    a = k
+    for j in range(k):
+        y, C, W = inverse_cdf(p_rows[j], float(u[j]))     # the row's own sample
+        lo = (C[xs[j] - 1] if xs[j] > 0 else 0.0) / W
+        hi = C[xs[j]] / W
+        uj = float(u[j])
+        margins.append(min(abs(uj - lo), abs(hi - uj)))
+        if y != xs[j]:
+            a = j
+            break
+    t, C, W = inverse_cdf(p_rows[a], float(u[a]))
+    lo = (C[t - 1] if t > 0 else 0.0) / W
+    hi = C[t] / W
+    p_x = [float(p_rows[i][xs[i]]) for i in range(k)]
+    return SampledRecord(a=a, tokens=xs[:a] + [t], p_x=p_x, q_x=[1.0] * k,
+                         theta=p_x, margins=margins, t=t, final_w=p_rows[a], final_C=C,
+                         final_W=W, final_u=float(u[a]),
+                         margin_final=min(float(u[a]) - lo, hi - float(u[a])))
+
+
 def sampled_request(p_rows, q_rows, drafts, u) -> SampledRecord:
     """One sampled request given its processed target rows p_0..p_k, draft
     rows q_0..q_{k-1} (float64 arrays or lazy row accessors), drafts
@@ -389,7 +427,7 @@ def verify(target, target_dtype, cu_seqlens, draft_tokens, uniforms=None, temper
         greedy = greedy_entry or is_greedy_temperature(T)
         kind = None if greedy else int(draft_kind[b])
 
-        if not greedy and (T == np.inf or kind not in (ONEHOT, LOGITS, PROBS)
+        if not greedy and (T == np.inf or kind not in (ONEHOT, LOGITS, PROBS, MATCH)
                            or (kind in (LOGITS, PROBS) and draft is None)):
             status[b] = ROW_BAD_PARAM
             continue
@@ -441,6 +479,18 @@ def verify(target, target_dtype, cu_seqlens, draft_tokens, uniforms=None, temper
             q_rows = _OneHotRows(xs, V)
 
         u = np.asarray(uniforms, dtype=np.float32)[c0:c0 + k + 1].astype(np.float64)
+        if kind == MATCH:
+            rec = match_request(p_rows, xs, u)
+            rec.near_tie = near
+            if not keep_cdf:
+                rec.final_w = rec.final_C = None
+            records[b] = rec
+            accepted[b] = rec.a
+            out_tokens[c0:c0 + rec.a + 1] = rec.tokens
+            for i in range(k):
+                p_at[d0 + i] = np.float32(rec.p_x[i])
+                q_at[d0 + i] = np.float32(1.0)
+            continue
         p_x = [float(p_rows[i][int(xs[i])]) for i in range(k)]
         q_x = [float(q_rows[i][int(xs[i])]) for i in range(k)]
         a, theta, margins = accept_scan(p_x, q_x, u)
@@ -521,7 +571,7 @@ def excusal(rec: SampledRecord, gpu_a: int, gpu_t: int, window: float = NEAR_TIE
 
 
 __all__ = [
-    "F32", "BF16", "ONEHOT", "LOGITS", "PROBS",
+    "F32", "BF16", "ONEHOT", "LOGITS", "PROBS", "MATCH", "match_request",
     "ROW_OK", "ROW_NONFINITE", "ROW_EMPTY", "ROW_BAD_K", "ROW_BAD_TOKEN", "ROW_BAD_PARAM",
     "widen", "process", "Dist", "argmax_lowest", "greedy_request", "accept_threshold",
     "accept_scan", "final_weights", "inverse_cdf", "final_draw", "sampled_request",
