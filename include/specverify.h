@@ -106,7 +106,14 @@ enum { SV_F32 = 0, SV_BF16 = 1 };
 enum {
   SV_DRAFT_ONEHOT = 0, /* argmax / n-gram drafts: q = e_x, no draft row is read */
   SV_DRAFT_LOGITS = 1, /* draft logits: the request's temperature and filters apply */
-  SV_DRAFT_PROBS = 2   /* cached draft probabilities: used as supplied */
+  SV_DRAFT_PROBS = 2,  /* cached draft probabilities: used as supplied */
+  SV_DRAFT_MATCH = 3   /* argmax drafts verified the way the PR page "FreeToken PR #836"
+                          (section "Design", rejection row) does it: every row j is
+                          sampled with its own uniform u[cu[b]+j] (inverse CDF, as the
+                          final draw below), drafts are accepted while each equals its
+                          row's sample, and the sample of the first other row (or of
+                          row k_b) is committed; no draft row is read.  Same law as
+                          SV_DRAFT_ONEHOT, different map from uniforms to tokens. */
 };
 
 /* per-request device status */

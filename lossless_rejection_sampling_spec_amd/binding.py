@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 
 SV_F32, SV_BF16 = 0, 1
-ONEHOT, LOGITS, PROBS = 0, 1, 2
+ONEHOT, LOGITS, PROBS, MATCH = 0, 1, 2, 3
 ROW_OK, ROW_NONFINITE, ROW_EMPTY, ROW_BAD_K, ROW_BAD_TOKEN, ROW_BAD_PARAM, ROW_INTERNAL = range(7)
 MAX_K = 63
 

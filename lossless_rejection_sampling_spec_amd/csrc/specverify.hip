@@ -388,8 +388,8 @@ __device__ __forceinline__ Req load_req(const Params& P, int b) {
   R.greedy = P.greedy_entry || !(R.T >= FLT_MIN);
   R.kind = R.greedy ? -1 : kind;
   R.bad_param = !R.greedy &&
-                (R.T == POS_INF || R.kind < SV_DRAFT_ONEHOT || R.kind > SV_DRAFT_PROBS ||
-                 (R.kind != SV_DRAFT_ONEHOT && P.draft == nullptr));
+                (R.T == POS_INF || R.kind < SV_DRAFT_ONEHOT || R.kind > SV_DRAFT_MATCH ||
+                 ((R.kind == SV_DRAFT_LOGITS || R.kind == SV_DRAFT_PROBS) && P.draft == nullptr));
   R.K = R.greedy ? 0 : K;
   R.P = R.greedy ? 1.f : Pp;
   if (R.K >= P.vocab) R.K = 0;
@@ -665,7 +665,7 @@ template <> __device__ __forceinline__ void apply_tau<uint16_t>(Seg<uint16_t>& s
 // -1.  par: the slot set of this chunk.  All threads return the same values.
 template <typename T>
 __device__ __forceinline__ CStat chunk_stats(Seg<T>& sg, bool greedy, float tau, float c, int xl,
-                                             int par, ProdShared& ps) {
+                                             int par, ProdShared& ps, bool before = false) {
   if (tau > NEG_INF) apply_tau<T>(sg, tau);
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -717,11 +717,21 @@ __device__ __forceinline__ CStat chunk_stats(Seg<T>& sg, bool greedy, float tau,
     const int xslot = ((xl / VEC) / WG) * VEC + xl % VEC;
     const int ix = ((int)threadIdx.x == owner) ? xslot : -1;
     if (own) {
+      if (before) {
+        // the terms of the elements that precede x in token order
 #pragma unroll
-      for (int i = 0; i < EPT; ++i) {
-        const float e = fterm(sg.at(i), c, mc);
-        acc += e;
-        accx += (i == ix) ? 0.f : e;
+        for (int i = 0; i < EPT; ++i) {
+          const float e = fterm(sg.at(i), c, mc);
+          acc += e;
+          accx += (strided_index<T>(i) < xl) ? e : 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+          const float e = fterm(sg.at(i), c, mc);
+          acc += e;
+          accx += (i == ix) ? 0.f : e;
+        }
       }
     }
   }
@@ -786,7 +796,9 @@ __device__ __forceinline__ void issue_task(const TT* trow, const TD* drow, bool 
 }
 
 // One producer task: the statistics of chunk c of the target row (is_d false)
-// or of the draft-logit row, kept in LDS (slot t) until the strip ends.
+// or of the draft-logit row, kept in LDS (slot t) until the strip ends.  For
+// the chunk holding the draft id x, the sum of the terms without x (or, for a
+// prefix-match request, of the terms before x) is kept as well.
 template <typename T, typename TT, typename TD, bool AL>
 __device__ __forceinline__ void produce_task(const Params& P, const Req& R, const Buf<TT, TD>& bf,
                                              bool is_d, int c, int x, float tau, int t,
@@ -799,7 +811,8 @@ __device__ __forceinline__ void produce_task(const Params& P, const Req& R, cons
   for (int i = 0; i < Seg<T>::NV; ++i) sg.q[i] = bf.q[i];
   finish_words<T>(n, AL, NEG_INF, [](int i) { return strided_off<T>(i); }, sg);
   const bool greedy = R.greedy && !is_d;
-  const CStat st = chunk_stats<T>(sg, greedy, tau, R.c, xin ? x - c0 : -1, t & 1, ps);
+  const CStat st = chunk_stats<T>(sg, greedy, tau, R.c, xin ? x - c0 : -1, t & 1, ps,
+                                  R.kind == SV_DRAFT_MATCH);
   if (threadIdx.x == 0) {
     ps.pub[t][0] = __float_as_uint(st.m);
     ps.pub[t][1] = greedy ? (uint32_t)st.arg : __float_as_uint(st.s);
@@ -837,7 +850,7 @@ __device__ __forceinline__ void produce(const Params& P, const Req& R, int b, in
   TD ldx_raw = TD(0);
   if (xs) {
     lx_raw = trow[x];
-    if (R.kind != SV_DRAFT_ONEHOT) ldx_raw = drow[x];
+    if (R.kind == SV_DRAFT_LOGITS || R.kind == SV_DRAFT_PROBS) ldx_raw = drow[x];
   }
 
   // two chunks in flight: chunk t+1 is requested before chunk t is reduced.
@@ -1166,7 +1179,7 @@ __device__ __forceinline__ void finalize(const Params& P, int b, int cu0, int k,
     // (also when a draft id is out of range: the statistics were still written)
     const int nA = (k + 1) * nc;
     const int nB = logits ? k * nc : 0;
-    const int rxw = sampled ? ((R.kind == SV_DRAFT_ONEHOT) ? 2 : 3) : 0;
+    const int rxw = sampled ? ((R.kind == SV_DRAFT_LOGITS || R.kind == SV_DRAFT_PROBS) ? 3 : 2) : 0;
     const int nC = k * rxw;
     int to = 0;
     for (int w = tid; w < nA + nB + nC; w += WG) {
@@ -1297,7 +1310,8 @@ __device__ __forceinline__ void finalize(const Params& P, int b, int cu0, int k,
         px = acc ? 1.0 : 0.0;
         qx = 1.0;
       } else {
-        px = exp2(((double)fs.lx[j] - (double)M) * R.ce) / S;
+        const double ex = exp2(((double)fs.lx[j] - (double)M) * R.ce);   // e_x in row-max units
+        px = ex / S;
         if (logits) {
           qx = exp2(((double)fs.dlx[j] - (double)Mq) * R.ce) / Sq;
         } else if (R.kind == SV_DRAFT_PROBS) {
@@ -1306,7 +1320,21 @@ __device__ __forceinline__ void finalize(const Params& P, int b, int cu0, int k,
         } else {
           qx = 1.0;
         }
-        acc = (double)fs.u[j] * qx < px;
+        if (R.kind == SV_DRAFT_MATCH) {
+          // the row's own sample is x iff u*S falls in x's interval of the
+          // running sum in token order: [mass before x, mass before x + e_x)
+          const int cx = x / CHUNK;
+          const float* mrow = st_m + j * nc;
+          const uint32_t* srow = st_s + j * nc;
+          double before = 0.0;
+          for (int c = 0; c < cx; ++c) before += (double)__uint_as_float(srow[c]);
+          if (mrow[cx] > NEG_INF)
+            before += (double)(fs.sx[j] * term(mrow[cx], M, R.c));
+          const double us = (double)fs.u[j] * S;
+          acc = ex > 0.0 && before <= us && us < before + ex;
+        } else {
+          acc = (double)fs.u[j] * qx < px;
+        }
       }
     }
     const uint64_t m_nf = __ballot(nonfin);
@@ -1323,7 +1351,8 @@ __device__ __forceinline__ void finalize(const Params& P, int b, int cu0, int k,
     fs.M[j] = M; fs.Mq[j] = Mq; fs.S[j] = S; fs.Sq[j] = Sq;
     // mode 2 (a rejection under a logit or probability draft): the helpers
     // finish the request, and its last helper is the only writer of its outputs
-    const bool resid = code == SV_ROW_OK && sampled && a < k && R.kind != SV_DRAFT_ONEHOT;
+    const bool resid = code == SV_ROW_OK && sampled && a < k &&
+                       (R.kind == SV_DRAFT_LOGITS || R.kind == SV_DRAFT_PROBS);
     if (resid && j < k) {
       fs.px[j] = (float)px;
       fs.qx[j] = (float)qx;
@@ -1345,7 +1374,7 @@ __device__ __forceinline__ void finalize(const Params& P, int b, int cu0, int k,
       fs.a = a;
       int mode = 0;   // 0 done, 1 draw from the target row here, 2 residual by the helpers
       if (code == SV_ROW_OK && sampled)
-        mode = (a == k || R.kind == SV_DRAFT_ONEHOT) ? 1 : 2;
+        mode = (a == k || R.kind == SV_DRAFT_ONEHOT || R.kind == SV_DRAFT_MATCH) ? 1 : 2;
       fs.mode = mode;
     }
   }
@@ -1362,7 +1391,10 @@ __device__ __forceinline__ void finalize(const Params& P, int b, int cu0, int k,
   if (mode == 1) {
     const int row = cu0 + a;
     const float tau = (P.thr_t && R.filt) ? thr_of(P.thr_t, row) : NEG_INF;
-    const int exclude = (a < k) ? fs.x[a] : -1;
+    // one-hot rejection: the residual is p without the draft; a prefix-match
+    // request commits row a's own sample, drawn with row a's uniform
+    const bool match = R.kind == SV_DRAFT_MATCH;
+    const int exclude = (a < k && !match) ? fs.x[a] : -1;
     // st_s holds the chunk sums already scaled to the row max
     const float* mrow = st_m + a * nc;
     const uint32_t* srow = st_s + a * nc;
@@ -1374,7 +1406,7 @@ __device__ __forceinline__ void finalize(const Params& P, int b, int cu0, int k,
       if (!(mrow[c] > NEG_INF)) return 0.0;
       return ex ? (double)(sxa * term(mrow[c], Ma, cf)) : (double)__uint_as_float(srow[c]);
     };
-    const int t = draw_target_row<TT, AL>(P, R, row, exclude, tau, (double)fs.u[k],
+    const int t = draw_target_row<TT, AL>(P, R, row, exclude, tau, (double)fs.u[match ? a : k],
                                           [=](int c) { return mrow[c]; }, mass, rc, sm, ds);
     if (tid == 0) P.out[row] = t;
     if (has_helpers(P, R)) helpers_none(P, b);
