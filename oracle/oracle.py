@@ -79,6 +79,7 @@ F32, BF16 = 0, 1
 ONEHOT, LOGITS, PROBS, MATCH = 0, 1, 2, 3
 # per-request status codes
 ROW_OK, ROW_NONFINITE, ROW_EMPTY, ROW_BAD_K, ROW_BAD_TOKEN = 0, 1, 2, 3, 4
+ROW_INTERNAL = 6
 
 NEAR_TIE = 1e-6
 
@@ -520,6 +521,90 @@ def verify(target, target_dtype, cu_seqlens, draft_tokens, uniforms=None, temper
 
 
 # --------------------------------------------------------------------------
+# after the verify: drain (commit) and acceptance accounting
+# --------------------------------------------------------------------------
+def drain(cu_seqlens, accepted, status, out_tokens, max_k=63):
+    """Commit the verified tokens of a batch and give back the unused slots.
+
+    Page "FreeToken PR #836", section "Design", drain row: commit
+    n = accepted + 1 tokens and roll back the unused slots of the k+1 verify
+    rows; the catalog page "Adding Speculative Decoding", "The four high-risk
+    coupling points" item 1 (accept all / some / none).
+
+    Per request b with k_b = cu[b+1] - cu[b] - 1 and a_b = accepted[b]:
+      n_b = a_b + 1 when status[b] is OK and 0 <= a_b <= k_b, else 0;
+      rollback_b = k_b + 1 - n_b, or 0 for a request whose offsets the verify
+      rejected (BAD_K: its slots are not known);
+      offsets = exclusive running sum of n; committed[offsets[b] + i] =
+      out_tokens[cu[b] + i] for i < n_b.
+    Returns (committed [offsets[-1]], offsets [B+1], rollback [B]), int32."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    B = cu.shape[0] - 1
+    acc = np.asarray(accepted, dtype=np.int64)
+    st = np.asarray(status, dtype=np.int64)
+    toks = np.asarray(out_tokens, dtype=np.int64)
+    n = np.zeros(B, dtype=np.int64)
+    rollback = np.zeros(B, dtype=np.int64)
+    for b in range(B):
+        if st[b] == ROW_BAD_K:
+            continue
+        k = int(cu[b + 1] - cu[b] - 1)
+        if st[b] == ROW_OK and 0 <= acc[b] <= k:
+            n[b] = acc[b] + 1
+        rollback[b] = k + 1 - n[b]
+    offsets = np.zeros(B + 1, dtype=np.int64)
+    for b in range(B):
+        offsets[b + 1] = offsets[b] + n[b]
+    committed = np.zeros(int(offsets[-1]), dtype=np.int64)
+    for b in range(B):
+        for i in range(int(n[b])):
+            committed[offsets[b] + i] = toks[cu[b] + i]
+    return committed.astype(np.int32), offsets.astype(np.int32), rollback.astype(np.int32)
+
+
+def accounting(cu_seqlens, accepted, status, ema, beta, threshold, k_low, k_high, counters):
+    """Acceptance accounting of one verify step and the next lookahead.
+
+    Counters (the Rust page, section "Production Pitfalls & Mitigation
+    Strategies", its metrics snippet): over the requests with status OK,
+    tokens generated += a_b + 1, tokens drafted += k_b, tokens accepted +=
+    a_b, and requests += 1 (so mean tokens per step = generated / requests,
+    acceptance rate = accepted / drafted; the catalog page, Acceptance bars
+    item 2).
+
+    Per request, the moving average of the acceptance rate and the adaptive
+    lookahead (same Rust page section, item 3: below a threshold such as
+    40 %, K drops from 5 to 2, and goes back up when the rate recovers):
+      r = a_b / k_b in float32; ema' = ema + beta * (r - ema), float32, in
+      that order (requests with k_b = 0 or a status other than OK keep ema);
+      k_next = k_low if ema' < threshold else k_high.
+    The moving average is float32 state, so it is computed in float32 here,
+    the precision in which the lookahead decision is taken.
+    Returns (ema' float32 [B], k_next int32 [B], counters int64 [4])."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    B = cu.shape[0] - 1
+    acc = np.asarray(accepted, dtype=np.int64)
+    st = np.asarray(status, dtype=np.int64)
+    ema_out = np.asarray(ema, dtype=np.float32).copy()
+    k_next = np.zeros(B, dtype=np.int32)
+    cnt = np.asarray(counters, dtype=np.int64).copy()
+    f32 = np.float32
+    for b in range(B):
+        k = int(cu[b + 1] - cu[b] - 1)
+        ok = st[b] == ROW_OK and 0 <= acc[b] <= k
+        if ok:
+            cnt[0] += acc[b] + 1
+            cnt[1] += k
+            cnt[2] += acc[b]
+            cnt[3] += 1
+            if k > 0:
+                r = f32(f32(acc[b]) / f32(k))
+                ema_out[b] = f32(ema_out[b] + f32(f32(beta) * f32(r - ema_out[b])))
+        k_next[b] = k_low if ema_out[b] < f32(threshold) else k_high
+    return ema_out, k_next, cnt
+
+
+# --------------------------------------------------------------------------
 # closed forms used as pins, and the comparison rule
 # --------------------------------------------------------------------------
 def expected_tokens_per_step(alpha: float, gamma: int) -> float:
@@ -573,8 +658,9 @@ def excusal(rec: SampledRecord, gpu_a: int, gpu_t: int, window: float = NEAR_TIE
 __all__ = [
     "F32", "BF16", "ONEHOT", "LOGITS", "PROBS", "MATCH", "match_request",
     "ROW_OK", "ROW_NONFINITE", "ROW_EMPTY", "ROW_BAD_K", "ROW_BAD_TOKEN", "ROW_BAD_PARAM",
+    "ROW_INTERNAL",
     "widen", "process", "Dist", "argmax_lowest", "greedy_request", "accept_threshold",
     "accept_scan", "final_weights", "inverse_cdf", "final_draw", "sampled_request",
     "SampledRecord", "verify", "BatchResult", "request_bounds", "is_greedy_temperature",
-    "expected_tokens_per_step", "acceptance_rate", "excusal",
+    "expected_tokens_per_step", "acceptance_rate", "excusal", "drain", "accounting",
 ]
