@@ -204,6 +204,53 @@ int spec_verify_sampled(const void* target_logits, int target_dtype, int64_t ld_
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Drain of a verified batch ("FreeToken PR #836", section "Design", drain row:
+ * commit n = accepted + 1 tokens and give back the unused slots; "Adding
+ * Speculative Decoding", "The four high-risk coupling points" item 1: accept
+ * all / some / none).  Run after a verify on the same stream, on its outputs.
+ * Per request b with k_b = cu[b+1] - cu[b] - 1 and a_b = accepted[b]:
+ *   n_b          = a_b + 1 if status[b] == SV_ROW_OK and 0 <= a_b <= k_b, else 0
+ *   rollback[b]  = k_b + 1 - n_b: verify slots (KV positions) to give back, or 0
+ *                  for SV_ROW_BAD_K or rows outside [0, total_rows)
+ *   commit_offsets[b] = n_0 + ... + n_{b-1}; commit_offsets[batch] = total
+ *   committed[commit_offsets[b] + i] = out_tokens[cu[b] + i] for i < n_b
+ *   cu_seqlens int32 [batch + 1], accepted / status int32 [batch],
+ *   out_tokens int32 [total_rows] (device, read);
+ *   committed int32 [total_rows], commit_offsets int32 [batch + 1],
+ *   rollback int32 [batch] (device, written; committed only up to the total,
+ *   never past total_rows).
+ *   Returns SV_OK, SV_ERR_NULL, SV_ERR_SHAPE (batch outside [1, 1024] or
+ *   total_rows < batch) or SV_ERR_LAUNCH.  Outputs must not alias inputs.
+ */
+int spec_verify_drain(const int32_t* cu_seqlens, const int32_t* accepted, const int32_t* status,
+                      const int32_t* out_tokens, int batch, int total_rows, int32_t* committed,
+                      int32_t* commit_offsets, int32_t* rollback, void* stream);
+
+/*
+ * Acceptance accounting of one verify step and the next lookahead.
+ * counters (int64 [4], device, accumulated in place) += over the requests with
+ * status OK and 0 <= a_b <= k_b: tokens generated (a_b + 1), tokens drafted
+ * (k_b), tokens accepted (a_b), requests (1) -- the three counters of the
+ * metrics in "Speculative Decoding in Custom LLM Servicing: Implementing Draft
+ * Models in Rust", "Production Pitfalls & Mitigation Strategies", plus the
+ * request count: acceptance rate = accepted / drafted, mean tokens per step =
+ * generated / requests ("Adding Speculative Decoding", Acceptance bars item 2).
+ * Per request, float32 throughout and in this order (no contraction):
+ *   r = a_b / k_b; ema_out[b] = ema_in[b] + beta * (r - ema_in[b])
+ *   (requests with k_b = 0 or not counted keep ema_in[b]);
+ *   k_next[b] = k_low if ema_out[b] < threshold else k_high
+ * -- the adaptive lookahead of the same Rust page section, item 3 (e.g. K from
+ * 5 to 2 below 40 %; k_low = 0 switches speculation off).  ema_out may equal
+ * ema_in.  Returns SV_OK, SV_ERR_NULL, SV_ERR_SHAPE (batch outside [1, 1024],
+ * beta outside [0, 1], NaN threshold, k_low or k_high outside [0, 63]) or
+ * SV_ERR_LAUNCH.
+ */
+int spec_verify_accounting(const int32_t* cu_seqlens, const int32_t* accepted,
+                           const int32_t* status, int batch, const float* ema_in, float* ema_out,
+                           float beta, float threshold, int k_low, int k_high, int32_t* k_next,
+                           int64_t* counters, void* stream);
+
+/*
  * spec_verify_sampled without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  It calls no hipMalloc, hipFree or other

@@ -58,6 +58,11 @@ def load_library(path: str) -> ctypes.CDLL:
     L.spec_verify_sampled.argtypes = [
         _vp, _i32, _i64, _vp, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
         _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+    L.spec_verify_drain.restype = _i32
+    L.spec_verify_drain.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp]
+    L.spec_verify_accounting.restype = _i32
+    L.spec_verify_accounting.argtypes = [_vp, _vp, _vp, _i32, _vp, _vp, ctypes.c_float,
+                                         ctypes.c_float, _i32, _i32, _vp, _vp, _vp]
     L.spec_verify_sampled_noalloc.restype = _i32
     L.spec_verify_sampled_noalloc.argtypes = [
         _vp, _i32, _i64, _vp, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -261,6 +266,45 @@ def verify_sampled_noalloc(target: torch.Tensor, draft: torch.Tensor | None,
         _ptr(q_at), _ptr(status), _stream(target.device))
     _raise(rc)
     return accepted, tokens, status, p_at, q_at
+
+
+def drain(cu_seqlens: torch.Tensor, accepted: torch.Tensor, status: torch.Tensor,
+          out_tokens: torch.Tensor):
+    """spec_verify_drain: (committed [total_rows], commit_offsets [B+1],
+    rollback [B]); only committed[:commit_offsets[B]] is written."""
+    dev = out_tokens.device
+    batch = cu_seqlens.numel() - 1
+    total_rows = out_tokens.numel()
+    for t, n in ((cu_seqlens, batch + 1), (accepted, batch), (status, batch), (out_tokens, total_rows)):
+        _check_vec(t, "drain input", torch.int32, n)
+    committed = torch.empty(total_rows, dtype=torch.int32, device=dev)
+    offsets = torch.empty(batch + 1, dtype=torch.int32, device=dev)
+    rollback = torch.empty(batch, dtype=torch.int32, device=dev)
+    _raise(lib().spec_verify_drain(_ptr(cu_seqlens), _ptr(accepted), _ptr(status), _ptr(out_tokens),
+                                   batch, total_rows, _ptr(committed), _ptr(offsets),
+                                   _ptr(rollback), _stream(dev)))
+    return committed, offsets, rollback
+
+
+def accounting(cu_seqlens: torch.Tensor, accepted: torch.Tensor, status: torch.Tensor,
+               ema: torch.Tensor, counters: torch.Tensor, *, beta: float = 0.1,
+               threshold: float = 0.4, k_low: int = 2, k_high: int = 5):
+    """spec_verify_accounting: updates `ema` (float32 [B]) and `counters`
+    (int64 [4]: generated, drafted, accepted, requests) in place and returns
+    k_next (int32 [B])."""
+    dev = ema.device
+    batch = cu_seqlens.numel() - 1
+    _check_vec(cu_seqlens, "cu_seqlens", torch.int32, batch + 1)
+    _check_vec(accepted, "accepted", torch.int32, batch)
+    _check_vec(status, "status", torch.int32, batch)
+    _check_vec(ema, "ema", torch.float32, batch)
+    _check_vec(counters, "counters", torch.int64, 4)
+    k_next = torch.empty(batch, dtype=torch.int32, device=dev)
+    _raise(lib().spec_verify_accounting(_ptr(cu_seqlens), _ptr(accepted), _ptr(status), batch,
+                                        _ptr(ema), _ptr(ema), float(beta), float(threshold),
+                                        int(k_low), int(k_high), _ptr(k_next), _ptr(counters),
+                                        _stream(dev)))
+    return k_next
 
 
 def workload_tensors(w, device) -> dict:

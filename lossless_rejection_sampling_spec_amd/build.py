@@ -10,7 +10,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "specverify.hip")
+SRC = [os.path.join(PKG, "csrc", "specverify.hip"), os.path.join(PKG, "csrc", "drain.hip")]
 INC = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libspecverify.so")
 # Test-only build: every wait between workgroups gives up after one poll, so
@@ -41,7 +41,7 @@ def hipcc() -> str:
 
 
 def _start(out: str, extra: list, verbose: bool):
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", INC, "-o", out + ".tmp", SRC]
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", INC, "-o", out + ".tmp", *SRC]
     if verbose:
         print(" ".join(cmd), flush=True)
     return subprocess.Popen(cmd)

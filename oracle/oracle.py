@@ -534,7 +534,8 @@ def drain(cu_seqlens, accepted, status, out_tokens, max_k=63):
     Per request b with k_b = cu[b+1] - cu[b] - 1 and a_b = accepted[b]:
       n_b = a_b + 1 when status[b] is OK and 0 <= a_b <= k_b, else 0;
       rollback_b = k_b + 1 - n_b, or 0 for a request whose offsets the verify
-      rejected (BAD_K: its slots are not known);
+      rejected (BAD_K: its slots are not known) or whose rows do not lie inside
+      the token buffer (the verify never reports such a request OK);
       offsets = exclusive running sum of n; committed[offsets[b] + i] =
       out_tokens[cu[b] + i] for i < n_b.
     Returns (committed [offsets[-1]], offsets [B+1], rollback [B]), int32."""
@@ -546,7 +547,7 @@ def drain(cu_seqlens, accepted, status, out_tokens, max_k=63):
     n = np.zeros(B, dtype=np.int64)
     rollback = np.zeros(B, dtype=np.int64)
     for b in range(B):
-        if st[b] == ROW_BAD_K:
+        if st[b] == ROW_BAD_K or not (0 <= cu[b] < cu[b + 1] <= toks.shape[0]):
             continue
         k = int(cu[b + 1] - cu[b] - 1)
         if st[b] == ROW_OK and 0 <= acc[b] <= k:

@@ -116,6 +116,20 @@ def test_noalloc_rejects_before_any_device_call():
                                          None) == 1
 
 
+def test_drain_and_accounting_validation():
+    L = binding.lib()
+    f = FAKE
+    assert L.spec_verify_drain(None, f, f, f, 2, 6, f, f, f, None) == 1
+    assert L.spec_verify_drain(f, f, f, f, 0, 6, f, f, f, None) == 2
+    assert L.spec_verify_drain(f, f, f, f, 1025, 2000, f, f, f, None) == 2
+    assert L.spec_verify_drain(f, f, f, f, 4, 3, f, f, f, None) == 2
+    assert L.spec_verify_accounting(f, f, f, 2, f, f, 0.1, 0.4, 2, 5, f, None, None) == 1
+    assert L.spec_verify_accounting(f, f, f, 2, f, f, 1.5, 0.4, 2, 5, f, f, None) == 2
+    assert L.spec_verify_accounting(f, f, f, 2, f, f, 0.1, float("nan"), 2, 5, f, f, None) == 2
+    assert L.spec_verify_accounting(f, f, f, 2, f, f, 0.1, 0.4, -1, 5, f, f, None) == 2
+    assert L.spec_verify_accounting(f, f, f, 2, f, f, 0.1, 0.4, 2, 64, f, f, None) == 2
+
+
 def test_workspace_init_null():
     assert binding.lib().spec_verify_workspace_init(None, 100, None) == 1
 

@@ -29,6 +29,9 @@ def test_drain_rejects_an_accepted_count_outside_the_request():
     cu = np.array([0, 3])
     c, o, r = oracle.drain(cu, np.array([5]), np.array([ROW_OK]), np.arange(3))
     assert c.tolist() == [] and o.tolist() == [0, 0] and r.tolist() == [3]
+    # rows outside the token buffer: nothing committed, nothing given back
+    c, o, r = oracle.drain(np.array([0, 5]), np.array([1]), np.array([ROW_OK]), np.arange(3))
+    assert c.tolist() == [] and o.tolist() == [0, 0] and r.tolist() == [0]
     # an INTERNAL request defines only its status: its accepted count is not trusted
     c, o, r = oracle.drain(cu, np.array([1]), np.array([oracle.ROW_INTERNAL]), np.arange(3))
     assert c.tolist() == [] and o.tolist() == [0, 0] and r.tolist() == [3]
