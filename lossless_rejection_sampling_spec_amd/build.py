@@ -17,6 +17,9 @@ LIB = os.path.join(PKG, "libspecverify.so")
 # the give-up path (SV_ROW_INTERNAL, the poisoned workspace) runs with every
 # kernel exiting normally.  Only the GPU tests load it.
 LIB_ONE_POLL = os.path.join(PKG, "libspecverify_onepoll.so")
+# The benchmark's streaming-read ceiling kernel (a measurement tool, not the verify).
+STREAM_SRC = os.path.join(PKG, "csrc", "stream_read.hip")
+LIB_STREAM = os.path.join(PKG, "libsvstream.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -40,17 +43,19 @@ def hipcc() -> str:
     return cand
 
 
-def _start(out: str, extra: list, verbose: bool):
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", INC, "-o", out + ".tmp", *SRC]
+def _start(out: str, extra: list, verbose: bool, sources=None):
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", INC, "-o", out + ".tmp", *(sources or SRC)]
     if verbose:
         print(" ".join(cmd), flush=True)
     return subprocess.Popen(cmd)
 
 
 def build(verbose: bool = True) -> str:
-    """Compile the library and its one-poll test build, side by side (every call)."""
+    """Compile the library, its one-poll test build and the benchmark's
+    streaming-read kernel, side by side (every call)."""
     jobs = [(LIB, _start(LIB, [], verbose)),
-            (LIB_ONE_POLL, _start(LIB_ONE_POLL, ["-DSV_SPIN_MAX=1"], verbose))]
+            (LIB_ONE_POLL, _start(LIB_ONE_POLL, ["-DSV_SPIN_MAX=1"], verbose)),
+            (LIB_STREAM, _start(LIB_STREAM, [], verbose, [STREAM_SRC]))]
     failed = [out for out, proc in jobs if proc.wait() != 0]
     if failed:
         raise RuntimeError(f"hipcc failed for {failed}")
