@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--no-stream", action="store_true", help="skip the streaming-read ceiling")
     ap.add_argument("--graph", action="store_true",
                     help="replay the headline steps from a captured HIP graph")
+    ap.add_argument("--only", type=int, choices=[c for c, _, _ in OTHERS],
+                    help="time only this other workload (for profiler runs); prints its record")
     return ap.parse_args()
 
 
@@ -307,6 +309,36 @@ def kernel_traffic():
     return TRAFFIC_BYTES.get(digest)
 
 
+def workload_record(cfg, label, wc, steps, warmup, reps):
+    """Time one of the other workloads and check the timed outputs."""
+    import numpy as np
+    from lossless_rejection_sampling_spec_amd import synth
+    ms_c, times_c, res_c = time_workload(wc, steps, warmup, reps)
+    tc = ms_c * 1e-3
+    ok = res_c["status"] == 0
+    acc = res_c["accepted"]
+    bytes_c = synth.algorithmic_bytes(wc, acc)
+    gb_c = bytes_c / tc / 1e9
+    return {"workload": label, "us_per_call": ms_c * 1e3, "rows_per_s": wc.total_rows / tc,
+            "tokens_committed_per_s": float(np.sum(acc[ok] + 1)) / tc,
+            "algorithmic_bytes_per_step": bytes_c, "achieved_GBps": gb_c,
+            "frac": gb_c / PEAK_HBM_GBPS, "step_ms_reps": times_c,
+            "parity_of_timed_outputs": parity(wc, res_c)}
+
+
+def only_workload(args):
+    import torch
+
+    from lossless_rejection_sampling_spec_amd import binding, synth
+    cfg, _, label = next(o for o in OTHERS if o[0] == args.only)
+    wc = synth.make(cfg, seed=args.seed)
+    torch.cuda.set_device(torch.device("cuda:0"))
+    binding.lib()
+    rec = workload_record(cfg, label, wc, args.steps, args.warmup, args.reps)
+    print(json.dumps({"only": cfg, **rec}), flush=True)
+    return 0
+
+
 def main() -> int:
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -320,6 +352,9 @@ def main() -> int:
 
     sys.path.insert(0, ROOT)
     from lossless_rejection_sampling_spec_amd import synth
+
+    if args.only is not None:
+        return only_workload(args)
 
     # inputs and the host-side baseline first: no GPU call has happened yet,
     # so the forked oracle workers inherit no device state
@@ -378,18 +413,7 @@ def main() -> int:
 
     per = {}
     for cfg, steps, label, wc in others:
-        ms_c, times_c, res_c = time_workload(wc, steps, 5, 3)
-        tc = ms_c * 1e-3
-        ok = res_c["status"] == 0
-        acc = res_c["accepted"]
-        bytes_c = synth.algorithmic_bytes(wc, acc)
-        gb_c = bytes_c / tc / 1e9
-        per[str(cfg)] = {
-            "workload": label, "us_per_call": ms_c * 1e3, "rows_per_s": wc.total_rows / tc,
-            "tokens_committed_per_s": float(np.sum(acc[ok] + 1)) / tc,
-            "algorithmic_bytes_per_step": bytes_c, "achieved_GBps": gb_c,
-            "frac": gb_c / PEAK_HBM_GBPS, "step_ms_reps": times_c,
-            "parity_of_timed_outputs": parity(wc, res_c)}
+        per[str(cfg)] = workload_record(cfg, label, wc, steps, 5, 3)
         torch.cuda.empty_cache()
     if per:
         line["per_config"] = per

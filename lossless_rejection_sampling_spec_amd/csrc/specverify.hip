@@ -69,6 +69,7 @@
 #include <algorithm>
 #include <cmath>
 #include <mutex>
+#include <type_traits>
 
 #include "specverify.h"
 
@@ -703,37 +704,45 @@ __device__ __forceinline__ CStat chunk_stats(Seg<T>& sg, bool greedy, float tau,
   // mc = m*c rounded once and the argument rounded once (one fused
   // multiply-add); the common factor exp2(m*c - mc) is put back exactly when the
   // thread's sum is scaled to the chunk max below.
+  // The rounding error of mc enters every term as a factor exp2(err) that the
+  // scale below takes out again; it stays harmless while |mc| < 2^30 (|err| <
+  // 64).  Beyond that (a huge |m|, or a tiny temperature) the thread takes the
+  // terms exp2((l - m) * c) instead, which cannot overflow for l <= m, and
+  // scales them to the chunk max by exp2((m - M) * c).
   float acc = 0.f, accx = 0.f;
   const bool own = m > NEG_INF && m < POS_INF;
   const float mc = m * c;
-  if (xl < 0) {
-    if (own) {
+  const bool fast = __builtin_fabsf(mc) < 1073741824.0f;
+  auto sum_terms = [&](auto tf) {
+    if (xl < 0) {
 #pragma unroll
-      for (int i = 0; i < EPT; ++i) acc += fterm(sg.at(i), c, mc);
-    }
-  } else {
-    constexpr int VEC = VT<T>::VEC;
-    const int owner = (xl / VEC) % WG;
-    const int xslot = ((xl / VEC) / WG) * VEC + xl % VEC;
-    const int ix = ((int)threadIdx.x == owner) ? xslot : -1;
-    if (own) {
+      for (int i = 0; i < EPT; ++i) acc += tf(sg.at(i));
+    } else {
+      constexpr int VEC = VT<T>::VEC;
+      const int owner = (xl / VEC) % WG;
+      const int xslot = ((xl / VEC) / WG) * VEC + xl % VEC;
+      const int ix = ((int)threadIdx.x == owner) ? xslot : -1;
       if (before) {
         // the terms of the elements that precede x in token order
 #pragma unroll
         for (int i = 0; i < EPT; ++i) {
-          const float e = fterm(sg.at(i), c, mc);
+          const float e = tf(sg.at(i));
           acc += e;
           accx += (strided_index<T>(i) < xl) ? e : 0.f;
         }
       } else {
 #pragma unroll
         for (int i = 0; i < EPT; ++i) {
-          const float e = fterm(sg.at(i), c, mc);
+          const float e = tf(sg.at(i));
           acc += e;
           accx += (i == ix) ? 0.f : e;
         }
       }
     }
+  };
+  if (own) {
+    if (fast) sum_terms([&](float v) { return fterm(v, c, mc); });
+    else sum_terms([&](float v) { return term(v, m, c); });
   }
   __syncthreads();
   float M = ps.m[par][0];
@@ -741,7 +750,8 @@ __device__ __forceinline__ CStat chunk_stats(Seg<T>& sg, bool greedy, float tau,
   for (int q = 1; q < NWAVE; ++q) M = fmax3nan(M, ps.m[par][q]);
   st.m = M;
   if (!(M > NEG_INF && M < POS_INF)) return st;   // empty chunk or a data fault
-  const double f = own ? (double)fterm(-M, c, -mc) : 0.0;   // exp2(mc - M*c)
+  const double f = !own ? 0.0 : fast ? (double)fterm(-M, c, -mc)   // exp2(mc - M*c)
+                                     : (double)term(m, M, c);
   const double ws = wave_sum((double)acc * f);
   double wsx = 0.0;
   if (xl >= 0) wsx = wave_sum((double)accx * f);
@@ -1976,162 +1986,466 @@ __global__ __launch_bounds__(WG, 4) void k_verify(const Params P) {
 }
 
 // ---------------------------------------------------------------------------
-// k_thresh: top-k / top-p thresholds (one workgroup per filtered row)
+// k_thresh: top-k / top-p thresholds, one workgroup of 1,024 threads per
+// filtered row
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t fkey(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0u;   // -0 and +0 are one value
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float keyf(uint32_t k) {
-  const uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
-  return __uint_as_float(u);
-}
+// A row's threshold is a radix select over order-preserving 32-bit keys of its
+// values (-0 folded into +0), 8 key bits per level: 2 levels for bf16 rows,
+// whose keys carry 16 bits, 4 for fp32.  Top-k counts values per digit; top-p
+// sums their masses exp2((v - M) c) rounded to integer multiples of 2^-40, so
+// that every order of summation gives the same bins.  A row of up to 131,072
+// bf16 or 65,536 fp32 values, 16-byte aligned, is read from HBM once and kept
+// in registers as keys (16 128-bit words per thread, two bf16 keys to a
+// 32-bit lane); every pass after the first runs from there.  Longer or
+// unaligned rows are read again for each pass.
+//
+// The passes are VALU-bound (a wave64 vector instruction takes 4 cycles), so
+// they are lean: the max pass is a packed 16-bit max and min over the keys,
+// the first count level adds every element (-inf and the padding past the row
+// land in digit 0, which is corrected only if the select reaches it), later
+// levels skip every element outside the chosen prefix.  A level's histogram
+// has HCOPY copies, one per lane of a half wave, so lanes of one LDS atomic
+// share an address only when they are 32 apart and agree on the digit; one
+// wave then picks the digit from suffix sums of the merged bins.
+constexpr int TW = 1024;          // threads of a threshold workgroup
+constexpr int TNW = TW / 64;
+constexpr int THR_NL = 16;        // 128-bit words per thread of a row kept in registers
+constexpr int HCOPY = 32;         // histogram copies
 
-constexpr double FIX = 1099511627776.0;   // 2^40: fixed-point unit of masses
+// Keys: the value's bits with the sign bit flipped for non-negative values
+// and every bit flipped for negative ones (unsigned order = value order);
+// bf16 keys are kept in the upper 16 bits of a 32-bit key.
+template <typename T> struct Keys;
+template <> struct Keys<uint16_t> {
+  static constexpr uint32_t NEG = 0x007f0000u;   // key of -inf (also the padding)
+  static constexpr uint32_t POS = 0xff800000u;   // key of +inf
+  // the two keys of a word of two bf16 values, packed
+  static __device__ __forceinline__ uint32_t of_word(uint32_t w) {
+    const uint32_t z = w & 0x7fff7fffu;
+    const uint32_t nz = (z + 0x7fff7fffu) & 0x80008000u;   // magnitude != 0, per half
+    w = (w & nz) | z;                                      // -0 -> +0
+    const uint32_t neg = (w >> 15) & 0x00010001u;
+    return w ^ (neg * 0x7fffu + 0x80008000u);
+  }
+  static __device__ __forceinline__ float value(uint32_t k) {
+    const uint32_t m = (uint32_t)((int32_t)k >> 31) & 0x7fffffffu;
+    return __uint_as_float(~(k ^ m) & 0xffff0000u);
+  }
+};
+template <> struct Keys<float> {
+  static constexpr uint32_t NEG = 0x007fffffu;
+  static constexpr uint32_t POS = 0xff800000u;
+  static __device__ __forceinline__ uint32_t of_word(uint32_t w) {
+    w = (w == 0x80000000u) ? 0u : w;
+    return w ^ ((uint32_t)((int32_t)w >> 31) | 0x80000000u);
+  }
+  static __device__ __forceinline__ float value(uint32_t k) {
+    const uint32_t m = (uint32_t)((int32_t)k >> 31) & 0x7fffffffu;
+    return __uint_as_float(~(k ^ m));
+  }
+};
+template <typename T>
+__device__ __forceinline__ uint4 keys_of(uint4 w) {
+  return make_uint4(Keys<T>::of_word(w.x), Keys<T>::of_word(w.y), Keys<T>::of_word(w.z),
+                    Keys<T>::of_word(w.w));
+}
 
 struct ThrShared {
-  unsigned cnt[NWAVE][256];
-  unsigned long long mass[NWAVE][256];
+  union {
+    unsigned c[256 * HCOPY];             // [digit][copy] counts
+    unsigned long long m[256 * HCOPY];   // [digit][copy] masses (units of 2^-40)
+  } h;
+  alignas(16) unsigned long long bins[256];   // merged bins of the level
+  uint32_t kw[2][TNW];
+  unsigned long long cw[TNW];
+  double target;                         // top-p: P times the total mass
+  unsigned long long above;              // count or mass above the digits chosen so far
+  unsigned long long upper;              // level 0 of top-k: values outside digit 0
   int digit;
-  unsigned long long rem;
-  double remd;
 };
 
-template <typename T>
-__device__ float row_threshold(const T* __restrict__ rp, int V, int levels, const Req& R,
-                               Smem& sm, ThrShared& th) {
-  const int tid = threadIdx.x;
-  const int w = tid >> 6;
-  // pass A: max and number of finite values
-  float m = NEG_INF;
-  int nfin = 0;
-  for (int e = tid; e < V; e += WG) {
-    const float v = to_f(rp[e]);
-    m = fmax3nan(m, v);
-    nfin += (v > NEG_INF && v < POS_INF) ? 1 : 0;
+// round(t * 2^40) for t in [0, 1]: t * 2^40 is exact in fp32, rintf rounds it
+// to nearest even (values of 2^23 and above are integers already), and the two
+// 32-bit halves of the integer are exact in fp32 too
+__device__ __forceinline__ unsigned long long fixmass(float t) {
+  const float s = __builtin_rintf(t * 1099511627776.0f);
+  const float hi = __builtin_floorf(s * 2.3283064365386963e-10f);
+  const float lo = s - hi * 4294967296.0f;
+  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// f(key) for the keys of one word of keys, in element order.
+template <typename T, typename F>
+__device__ __forceinline__ void each_key(const uint4& w, F& f) {
+  const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    if constexpr (sizeof(T) == 4) {
+      f(d[h]);
+    } else {
+      f(d[h] << 16);
+      f(d[h] & 0xffff0000u);
+    }
   }
-  const float M = block_max(m, sm);
-  // sum of counts via the fp64 reduction (exact for counts < 2^53)
-  const int NF = (int)block_sum_d((double)nfin, sm);
-  if (!(M > NEG_INF && M < POS_INF)) return NEG_INF;   // faults are reported by the row pass
-  const bool do_k = R.K > 0 && R.K < NF;
+}
+
+// Word g of a row (elements [g*VEC, g*VEC + VEC)).  al: one 128-bit load from
+// an offset clamped to the row's last word (thr_mask then puts -inf past
+// element V); otherwise element loads with -inf past V.
+template <typename T>
+__device__ __forceinline__ uint4 thr_word(const T* __restrict__ rp, int g, int V, bool al) {
+  constexpr int VEC = VT<T>::VEC;
+  const int e0 = g * VEC;
+  if (!al) return load_word_scalar<T>(rp, e0, V, NEG_INF);
+  const int last = ((V - 1) / VEC) * VEC;
+  return *reinterpret_cast<const uint4*>(rp + min(e0, last));
+}
+template <typename T>
+__device__ __forceinline__ uint4 thr_mask(uint4 w, int g, int V) {
+  constexpr int VEC = VT<T>::VEC;
+  const int e0 = g * VEC;
+  return (e0 + VEC > V) ? mask_tail<T>(w, V - e0, fill_bits<T>(NEG_INF)) : w;
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// 64-bit DPP moves (two 32-bit moves; lanes without a source read 0) and the
+// wave's inclusive sum in lane order, with no lane-address registers (the
+// level loop would keep those live across every pass)
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long x) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, CTRL, ROWS, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), CTRL, ROWS, 0xf, false);
+  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ __forceinline__ unsigned long long wave_scan_u64(unsigned long long x) {
+  x += dpp_u64<0x111>(x);         // row_shr:1
+  x += dpp_u64<0x112>(x);         // row_shr:2
+  x += dpp_u64<0x114>(x);         // row_shr:4
+  x += dpp_u64<0x118>(x);         // row_shr:8
+  x += dpp_u64<0x142, 0xa>(x);    // row_bcast:15
+  x += dpp_u64<0x143, 0xc>(x);    // row_bcast:31
+  return x;
+}
+__device__ __forceinline__ unsigned long long readlane_u64(unsigned long long x, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Running max and min of the keys of a word of keys (bf16: per 16-bit half).
+template <typename T>
+__device__ __forceinline__ void key_range(const uint4& w, uint32_t& mx, uint32_t& mn) {
+  const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    if constexpr (sizeof(T) == 4) {
+      mx = max(mx, d[h]);
+      mn = min(mn, d[h]);
+    } else {
+      const u16x2 a = __builtin_bit_cast(u16x2, d[h]);
+      mx = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, mx), a));
+      mn = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, mn), a));
+    }
+  }
+}
+
+__device__ __forceinline__ void thr_block_range(uint32_t& mx, uint32_t& mn, ThrShared& th) {
+  // unsigned order through signed values with the top bit flipped
+  int sx = (int)(mx ^ 0x80000000u), sn = (int)(mn ^ 0x80000000u);
+  sx = wave_reduce_rows(sx, [](int a, int b) { return max(a, b); });
+  sn = wave_reduce_rows(sn, [](int a, int b) { return min(a, b); });
+  mx = (uint32_t)sx ^ 0x80000000u;
+  mn = (uint32_t)sn ^ 0x80000000u;
+  if ((threadIdx.x & 63) == 0) {
+    th.kw[0][threadIdx.x >> 6] = mx;
+    th.kw[1][threadIdx.x >> 6] = mn;
+  }
+  __syncthreads();
+  mx = th.kw[0][0];
+  mn = th.kw[1][0];
+#pragma unroll
+  for (int q = 1; q < TNW; ++q) {
+    mx = max(mx, th.kw[0][q]);
+    mn = min(mn, th.kw[1][q]);
+  }
+}
+
+// Sum of a count over the workgroup (exact in fp64: counts stay below 2^53).
+__device__ __forceinline__ unsigned long long thr_block_sum(unsigned long long x, ThrShared& th) {
+  x = (unsigned long long)wave_reduce_rows((double)x, [](double a, double b) { return a + b; });
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) th.cw[threadIdx.x >> 6] = x;
+  __syncthreads();
+  unsigned long long r = 0ull;
+#pragma unroll
+  for (int q = 0; q < TNW; ++q) r += th.cw[q];
+  return r;
+}
+
+__device__ __forceinline__ void clear_bins(ThrShared& th) {
+  uint4* hz = reinterpret_cast<uint4*>(&th.h);
+  constexpr int NZ = (int)(sizeof(th.h) / 16);
+  for (int i = threadIdx.x; i < NZ; i += TW) hz[i] = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
+}
+
+// Merge the copies of each bin into th.bins (thread t: bin t/4, a quarter of
+// the copies, read as 128-bit words from one base address).
+template <bool MASS>
+__device__ __forceinline__ void merge_bins(ThrShared& th) {
+  static_assert(HCOPY == 32, "a quarter of the copies is eight words");
+  const int tid = threadIdx.x;
+  const int d = tid >> 2, part = tid & 3;
+  unsigned long long s = 0ull;
+  if constexpr (MASS) {
+    const ulonglong2* p = reinterpret_cast<const ulonglong2*>(&th.h.m[d * HCOPY + part * 8]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const ulonglong2 v = p[q];
+      s += v.x + v.y;
+    }
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(&th.h.c[d * HCOPY + part * 8]);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint4 v = p[q];
+      s += (unsigned long long)v.x + v.y + v.z + v.w;
+    }
+  }
+  s += dpp_u64<DPP_XOR1>(s);
+  s += dpp_u64<DPP_XOR2>(s);
+  if (part == 0) th.bins[d] = s;
+  __syncthreads();
+}
+
+// Wave 0 picks the highest digit whose bins from the top, with everything
+// above from earlier levels, reach the goal: K values (counts) or the target
+// mass (masses; at level 0 the target is P times the level's total).
+template <bool MASS>
+__device__ __forceinline__ void pick_digit(ThrShared& th, int lev, unsigned K, float Pp) {
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const int l = tid;
+    // this lane's digits 255 - 4l down to 252 - 4l
+    const ulonglong2* bp = reinterpret_cast<const ulonglong2*>(&th.bins[252 - 4 * l]);
+    const ulonglong2 b01 = bp[0], b23 = bp[1];
+    const unsigned long long bb[4] = {b23.y, b23.x, b01.y, b01.x};
+    const unsigned long long ls = bb[0] + bb[1] + bb[2] + bb[3];
+    const unsigned long long inc = wave_scan_u64(ls);
+    const unsigned long long total = readlane_u64(inc, 63);
+    const unsigned long long base = lev == 0 ? 0ull : th.above;
+    const double tgt = lev == 0 ? (double)Pp * (double)total : th.target;
+    unsigned long long c = base + inc - ls;
+    int first = 4;
+    unsigned long long at = 0ull;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const unsigned long long ci = c + bb[i];
+      const bool hit = MASS ? ((double)ci >= tgt) : (ci >= (unsigned long long)K);
+      if (first == 4 && hit) {
+        first = i;
+        at = c;
+      }
+      c = ci;
+    }
+    const uint64_t msk = __ballot(first < 4);
+    const int src = msk ? (int)__builtin_ctzll(msk) : 0;
+    const int f = __builtin_amdgcn_readlane(first, src);
+    const unsigned long long ab = readlane_u64(at, src);
+    if (l == 0) {
+      th.digit = msk ? 255 - (4 * src + f) : 0;
+      th.above = msk ? ab : base;
+      if (lev == 0) th.target = tgt;
+    }
+  }
+  __syncthreads();
+}
+
+template <typename T, bool REG>
+__device__ __forceinline__ float row_threshold(const T* __restrict__ rp, int V, bool al,
+                                               const Req& R, ThrShared& th) {
+  constexpr int VEC = VT<T>::VEC;
+  constexpr int LEVELS = sizeof(T) == 2 ? 2 : 4;
+  constexpr uint32_t KNEG = Keys<T>::NEG;
+  const int tid = threadIdx.x;
+  const int cp = tid & (HCOPY - 1);
+  uint4 w[REG ? THR_NL : 1];
+  if constexpr (REG) {
+    // word i of every thread covers elements [i*TW*VEC, (i+1)*TW*VEC): only the
+    // one that holds the row's end needs per-lane clamps and masks (the
+    // conditions are uniform)
+    const T* base = rp + tid * VEC;
+    const uint32_t nb = fill_bits<T>(NEG_INF);
+    const uint32_t nw = sizeof(T) == 4 ? nb : (nb | (nb << 16));
+#pragma unroll
+    for (int i = 0; i < THR_NL; ++i) {
+      const int g0 = i * TW * VEC;
+      if (g0 + TW * VEC <= V) w[i] = *reinterpret_cast<const uint4*>(base + g0);
+      else if (g0 < V) w[i] = thr_word<T>(rp, i * TW + tid, V, true);
+      else w[i] = make_uint4(nw, nw, nw, nw);
+    }
+#pragma unroll
+    for (int i = 0; i < THR_NL; ++i) {
+      const int g0 = i * TW * VEC;
+      if (g0 + TW * VEC > V && g0 < V) w[i] = thr_mask<T>(w[i], i * TW + tid, V);
+      w[i] = keys_of<T>(w[i]);
+    }
+  }
+  // words(f): f(word of keys) for every word of the thread: from the
+  // registers, or read again eight at a time (padding past the row: -inf)
+  auto words = [&](auto&& f) {
+    if constexpr (REG) {
+      // the words pass through an empty asm statement first: what a pass
+      // derives from them does not depend on the level, and the compiler
+      // would otherwise keep it for every element across the levels
+#pragma unroll
+      for (int i = 0; i < THR_NL; ++i)
+        asm volatile("" : "+v"(w[i].x), "+v"(w[i].y), "+v"(w[i].z), "+v"(w[i].w));
+#pragma unroll
+      for (int i = 0; i < THR_NL; ++i) f(w[i]);
+    } else {
+      const int ng = (V + VEC - 1) / VEC;
+      for (int g0 = tid; g0 < ng; g0 += 8 * TW) {
+        uint4 q[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = thr_word<T>(rp, min(g0 + i * TW, ng - 1), V, al);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (g0 + i * TW < ng) f(keys_of<T>(thr_mask<T>(q[i], g0 + i * TW, V)));
+        }
+      }
+    }
+  };
+  auto each = [&](auto&& f) { words([&](const uint4& x) { each_key<T>(x, f); }); };
+
+  // max and min key: a NaN (keys above +inf's or below -inf's), +inf, or a
+  // row of -inf leaves the row unfiltered (faults are reported by the row pass)
+  uint32_t kmax = 0u, kmin = 0xffffffffu;
+  words([&](const uint4& x) { key_range<T>(x, kmax, kmin); });
+  if constexpr (sizeof(T) == 2) {
+    kmax = max(kmax << 16, kmax & 0xffff0000u);
+    kmin = min(kmin << 16, kmin & 0xffff0000u);
+  }
+  thr_block_range(kmax, kmin, th);
+  if (kmax >= Keys<T>::POS || kmin < KNEG || kmax <= KNEG) return NEG_INF;
+  const float M = Keys<T>::value(kmax);
+
+  bool do_k = R.K > 0;
   const bool do_p = R.P > 0.f && R.P < 1.f;
   uint32_t tau_key = 0u;   // keep everything
   if (do_k) {
+    const unsigned K = (unsigned)R.K;
     uint32_t prefix = 0u, pmask = 0u;
-    unsigned remaining = (unsigned)R.K;
-    for (int lev = 0; lev < levels; ++lev) {
+    unsigned long long ninf = 0ull;   // -inf values and padding (counted only when needed)
+#pragma unroll
+    for (int lev = 0; lev < LEVELS; ++lev) {
       const int shift = 24 - 8 * lev;
-      for (int d = tid; d < 256 * NWAVE; d += WG) (&th.cnt[0][0])[d] = 0u;
-      __syncthreads();
-      for (int e = tid; e < V; e += WG) {
-        const float v = to_f(rp[e]);
-        if (!(v > NEG_INF)) continue;
-        const uint32_t key = fkey(v);
-        if ((key & pmask) != prefix) continue;
-        atomicAdd(&th.cnt[w][(key >> shift) & 255u], 1u);
+      clear_bins(th);
+      if (lev == 0) {
+        each([&](uint32_t k) { atomicAdd(&th.h.c[(k >> 24) * HCOPY + cp], 1u); });
+      } else {
+        each([&](uint32_t k) {
+          if ((k & pmask) == prefix) atomicAdd(&th.h.c[((k >> shift) & 255u) * HCOPY + cp], 1u);
+        });
       }
       __syncthreads();
-      if (tid == 0) {
-        unsigned above = 0u;
-        int dsel = 0;
-        for (int d = 255; d >= 0; --d) {
-          unsigned cd = 0u;
-          for (int q = 0; q < NWAVE; ++q) cd += th.cnt[q][d];
-          if (above + cd >= remaining) { dsel = d; break; }
-          above += cd;
+      merge_bins<false>(th);
+      if (lev == 0) {
+        // digit 0 holds -inf and the padding: count them only if the select
+        // can reach digit 0 or K may not be below the number of finite values
+        if (tid < 64) {
+          const ulonglong2* bp = reinterpret_cast<const ulonglong2*>(&th.bins[4 * tid]);
+          const ulonglong2 b01 = bp[0], b23 = bp[1];
+          unsigned long long u = (tid ? b01.x : 0ull) + b01.y + b23.x + b23.y;
+          u = (unsigned long long)wave_reduce_rows((double)u, [](double a, double b) { return a + b; });
+          if (tid == 0) th.upper = u;
         }
-        th.digit = dsel;
-        th.rem = remaining - above;
+        __syncthreads();
+        if (th.upper <= (unsigned long long)K) {
+          unsigned long long n = 0ull;
+          each([&](uint32_t k) { n += (k == KNEG) ? 1ull : 0ull; });
+          ninf = thr_block_sum(n, th);
+          const unsigned long long finite = th.upper + th.bins[0] - ninf;
+          if ((unsigned long long)K >= finite) {
+            do_k = false;
+            break;
+          }
+        }
       }
+      // -inf values still inside the prefix are not candidates
+      if (tid == 0 && ninf != 0ull && (KNEG & pmask) == prefix) th.bins[(KNEG >> shift) & 255u] -= ninf;
       __syncthreads();
-      remaining = (unsigned)th.rem;
+      pick_digit<false>(th, lev, K, 0.f);
       prefix |= (uint32_t)th.digit << shift;
       pmask |= 255u << shift;
     }
-    tau_key = prefix;
+    if (do_k) tau_key = prefix;
   }
   if (do_p) {
-    const float tau_k = do_k ? keyf(tau_key) : NEG_INF;
+    // the top-k set, -inf excluded (its masses are 0 anyway)
+    const uint32_t kfloor = do_k ? tau_key : KNEG + 1u;
     uint32_t prefix = 0u, pmask = 0u;
-    double target = 0.0;
-    for (int lev = 0; lev < levels; ++lev) {
+#pragma unroll
+    for (int lev = 0; lev < LEVELS; ++lev) {
       const int shift = 24 - 8 * lev;
-      for (int d = tid; d < 256 * NWAVE; d += WG) (&th.mass[0][0])[d] = 0ull;
+      clear_bins(th);
+      auto add = [&](uint32_t k) {
+        const unsigned long long fx = fixmass(term(Keys<T>::value(k), M, R.c));
+        atomicAdd(&th.h.m[((k >> shift) & 255u) * HCOPY + cp], fx);
+      };
+      each([&](uint32_t k) {
+        if (k >= kfloor && (k & pmask) == prefix) add(k);
+      });
       __syncthreads();
-      for (int e = tid; e < V; e += WG) {
-        const float v = to_f(rp[e]);
-        if (!(v > NEG_INF) || v < tau_k) continue;
-        const uint32_t key = fkey(v);
-        if ((key & pmask) != prefix) continue;
-        const unsigned long long fx =
-            (unsigned long long)__double2ll_rn((double)term(v, M, R.c) * FIX);
-        atomicAdd(&th.mass[w][(key >> shift) & 255u], fx);
-      }
-      __syncthreads();
-      {
-        unsigned long long sacc = 0ull;
-        for (int q = 0; q < NWAVE; ++q) sacc += th.mass[q][tid];
-        __syncthreads();
-        th.mass[0][tid] = sacc;
-      }
-      __syncthreads();
-      if (tid == 0) {
-        unsigned long long Z = 0ull;
-        for (int d = 0; d < 256; ++d) Z += th.mass[0][d];
-        if (lev == 0) target = (double)R.P * (double)Z;
-        else target = th.remd;
-        double above = 0.0;
-        int dsel = -1, lastnz = -1;
-        for (int d = 255; d >= 0; --d) {
-          const unsigned long long td = th.mass[0][d];
-          if (td == 0ull) continue;
-          lastnz = d;
-          if (above + (double)td >= target) { dsel = d; break; }
-          above += (double)td;
-        }
-        if (dsel < 0) dsel = (lastnz >= 0) ? lastnz : 0;
-        th.digit = dsel;
-        th.remd = target - above;
-      }
-      __syncthreads();
+      merge_bins<true>(th);
+      pick_digit<true>(th, lev, 0u, R.P);
       prefix |= (uint32_t)th.digit << shift;
       pmask |= 255u << shift;
     }
     tau_key = prefix > tau_key ? prefix : tau_key;
   }
   if (!do_k && !do_p) return NEG_INF;
-  return keyf(tau_key);
+  return Keys<T>::value(tau_key);
+}
+
+template <typename T>
+__device__ __forceinline__ float thr_row(const T* __restrict__ rp, int64_t ld, int V, const Req& R,
+                                         ThrShared& th) {
+  const bool al = (((uintptr_t)rp & 15) == 0) && (((ld * (int64_t)sizeof(T)) & 15) == 0);
+  if (al && V <= THR_NL * TW * VT<T>::VEC) return row_threshold<T, true>(rp, V, true, R, th);
+  return row_threshold<T, false>(rp, V, al, R, th);
 }
 
 template <typename TT, typename TD, int E>
-__global__ __launch_bounds__(WG) void k_thresh(const Params P) {
-  __shared__ Smem sm;
+__global__ __launch_bounds__(TW) void k_thresh(const Params P) {
   __shared__ ThrShared th;
   int bid = blockIdx.x;
   const int side = bid & 1;   // 0 target row, 1 draft row
   bid >>= 1;
   const int j = bid % (P.max_k + 1);
   const int b = bid / (P.max_k + 1);
-  const int cu0 = P.cu[b];
-  const int cu1 = P.cu[b + 1];
+  // scalar loads decide which workgroups have a row; only those check the
+  // offsets the way k_verify does (rows of an invalid request may be another's)
+  const int cu0 = ldu(P.cu + b);
+  const int cu1 = ldu(P.cu + b + 1);
   const int k = cu1 - cu0 - 1;
-  // the verdict k_verify gives: rows of an invalid request may be another's
-  if (j > k || !offsets_ok<E>(P, b, cu0, cu1)) return;
   const Req R = load_req(P, b);
-  if (R.greedy || R.bad_param || !R.filt) return;
+  if (j > k || R.greedy || R.bad_param || !R.filt) return;
   if (side == 1 && (R.kind != SV_DRAFT_LOGITS || j >= k)) return;
+  if (!offsets_ok<E>(P, b, cu0, cu1)) return;
+  u64* out = side == 0 ? P.thr_t + cu0 + j : P.thr_d + (cu0 - b + j);
   float tau;
-  if (side == 0) {
-    const TT* rp = (const TT*)P.target + (int64_t)(cu0 + j) * P.ld_t;
-    tau = row_threshold<TT>(rp, P.vocab, sizeof(TT) == 2 ? 2 : 4, R, sm, th);
-    if (threadIdx.x == 0) P.thr_t[cu0 + j] = (u64)__float_as_uint(tau);
+  if constexpr (std::is_same<TT, TD>::value) {   // one copy of the code for both sides
+    const TT* rp = side == 0 ? (const TT*)P.target + (int64_t)(cu0 + j) * P.ld_t
+                             : (const TT*)P.draft + (int64_t)(cu0 - b + j) * P.ld_d;
+    tau = thr_row<TT>(rp, side == 0 ? P.ld_t : P.ld_d, P.vocab, R, th);
+  } else if (side == 0) {
+    tau = thr_row<TT>((const TT*)P.target + (int64_t)(cu0 + j) * P.ld_t, P.ld_t, P.vocab, R, th);
   } else {
-    const TD* rp = (const TD*)P.draft + (int64_t)(cu0 - b + j) * P.ld_d;
-    tau = row_threshold<TD>(rp, P.vocab, sizeof(TD) == 2 ? 2 : 4, R, sm, th);
-    if (threadIdx.x == 0) P.thr_d[cu0 - b + j] = (u64)__float_as_uint(tau);
+    tau = thr_row<TD>((const TD*)P.draft + (int64_t)(cu0 - b + j) * P.ld_d, P.ld_d, P.vocab, R, th);
   }
+  if (threadIdx.x == 0) *out = (u64)__float_as_uint(tau);
 }
 
 __global__ void k_fill_zero(uint4* p, size_t n16, unsigned char* tail, size_t ntail) {
@@ -2193,9 +2507,9 @@ static int launch_all(Params P, bool sampled, bool filters, bool aligned, hipStr
   if (filters) {
     const long long g0 = (long long)P.batch * (P.max_k + 1) * 2;
     if (P.batch <= 64)
-      hipLaunchKernelGGL((k_thresh<TT, TD, 1>), dim3((unsigned)g0), dim3(WG), 0, st, P);
+      hipLaunchKernelGGL((k_thresh<TT, TD, 1>), dim3((unsigned)g0), dim3(TW), 0, st, P);
     else
-      hipLaunchKernelGGL((k_thresh<TT, TD, 16>), dim3((unsigned)g0), dim3(WG), 0, st, P);
+      hipLaunchKernelGGL((k_thresh<TT, TD, 16>), dim3((unsigned)g0), dim3(TW), 0, st, P);
   }
   if (P.batch <= 64) {
     if (aligned)

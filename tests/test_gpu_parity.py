@@ -286,6 +286,87 @@ def test_edge_filters():
                             ddtype=dtype, top_k=K, top_p=P, u=[0.3, 0.6, 0.7]))
 
 
+def test_edge_threshold_paths():
+    """The paths of the top-k / top-p select: rows read again for each pass
+    instead of kept in registers (bf16 beyond 131,072 values, fp32 beyond
+    65,536, rows that are not 16-byte aligned), rows that are mostly -inf (K at,
+    below and above the number of finite values, and a K-th largest among huge
+    negative values next to -inf), and signed-zero ties at the cut."""
+    rng = np.random.default_rng(11)
+
+    def run(rows, draft, dtype, K, P, **kw):
+        xs = [int(np.argmax(d)) for d in np.atleast_2d(draft)]
+        say(f"threshold paths V={rows.shape[1]} dtype={dtype} K={K} P={P} {kw}")
+        check_edge(_one(rows, T=0.8, kind=synth.LOGITS, drafts=xs, draft=draft, dtype=dtype,
+                        ddtype=dtype, top_k=K, top_p=P, u=[0.4, 0.6][:rows.shape[0]], **kw))
+
+    for V, dtype in ((140000, synth.BF16), (70000, synth.F32)):
+        rows = np.round(rng.normal(0, 2, size=(2, V)), 2)
+        draft = rows[:1] + rng.normal(0, 0.3, size=(1, V))
+        for K, P in ((20, 1.0), (0, 0.9), (50, 0.95)):
+            run(rows, draft, dtype, K, P)
+    V = 9000
+    rows = np.round(rng.normal(0, 2, size=(2, V)), 1)
+    draft = rows[:1] + rng.normal(0, 0.3, size=(1, V))
+    for dtype in (synth.BF16, synth.F32):
+        run(rows, draft, dtype, 30, 0.9, ld=V + 3, offset=3)
+
+    V = 3000
+    rows = np.full((2, V), -np.inf)
+    live = rng.choice(V, size=10, replace=False)
+    rows[:, live] = rng.normal(0, 1.5, size=(2, 10))
+    draft = rows[:1] + np.where(np.isfinite(rows[:1]), 0.2, 0.0)
+    for dtype in (synth.BF16, synth.F32):
+        for K, P in ((9, 1.0), (10, 1.0), (11, 0.8), (50, 0.8), (3, 0.7)):
+            run(rows, draft, dtype, K, P)
+    # the K-th largest among values next to the most negative finite ones
+    rows = np.full((2, V), -np.inf)
+    rows[:, live[:5]] = rng.uniform(0, 1, size=(2, 5))
+    huge = rng.choice(np.setdiff1d(np.arange(V), live), size=20, replace=False)
+    rows[:, huge] = -rng.uniform(2.0e38, 3.0e38, size=(2, 20))
+    draft = rows[:1].copy()
+    for dtype in (synth.BF16, synth.F32):
+        for K, P in ((15, 1.0), (25, 1.0), (15, 0.5)):
+            run(rows, draft, dtype, K, P)
+
+    # signed zeros at the cut: 30 ones, 20 zeros of each sign, the rest -1
+    V = 5000
+    rows = np.full((2, V), -1.0)
+    perm = rng.permutation(V)
+    rows[:, perm[:30]] = 1.0
+    rows[:, perm[30:50]] = 0.0
+    rows[:, perm[50:70]] = -0.0
+    draft = rows[:1] + np.round(rng.normal(0, 0.2, size=(1, V)), 1)
+    for dtype in (synth.BF16, synth.F32):
+        for K, P in ((50, 1.0), (31, 1.0), (0, 0.6), (60, 0.9)):
+            run(rows, draft, dtype, K, P)
+
+
+def test_edge_tiny_temperature_and_huge_logits():
+    """1/T near the top of the fp32 range (T just above FLT_MIN) with ordinary
+    logits, and ordinary T with logits near -FLT_MAX: a row max times 1/T
+    overflows fp32, and the statistics must still follow the oracle."""
+    rng = np.random.default_rng(12)
+    V, k = 20000, 2
+    rows = rng.normal(0, 20, size=(k + 1, V))
+    draft = rows[:k] + rng.normal(0, 1.0, size=(k, V))
+    xs = [int(np.argmax(d)) for d in draft]
+    for T in (2e-38, 1e-30):
+        for dtype in (synth.BF16, synth.F32):
+            say(f"tiny T={T} dtype={dtype}")
+            check_edge(_one(rows, T=T, kind=synth.LOGITS, drafts=xs, draft=draft, dtype=dtype,
+                            ddtype=dtype, u=[0.3, 0.7, 0.5]))
+            check_edge(_one(rows, T=T, kind=synth.ONEHOT, drafts=xs, dtype=dtype,
+                            u=[0.3, 0.7, 0.5]))
+    huge = -3.0e38 + rng.uniform(0, 1e38, size=(k + 1, V))
+    hd = huge[:k] + rng.uniform(0, 1e37, size=(k, V))
+    xs = [int(np.argmax(d)) for d in hd]
+    for dtype in (synth.BF16, synth.F32):
+        say(f"huge negative logits dtype={dtype}")
+        check_edge(_one(huge, T=0.7, kind=synth.LOGITS, drafts=xs, draft=hd, dtype=dtype,
+                        ddtype=dtype, u=[0.3, 0.7, 0.5]))
+
+
 def test_bitwise_determinism_and_batch_invariance():
     w = synth.make(3, seed=7, batch=20, vocab=20000)
     a = gpu_sampled(w)
