@@ -1989,78 +1989,85 @@ __global__ __launch_bounds__(WG, 4) void k_verify(const Params P) {
 // k_thresh: top-k / top-p thresholds, one workgroup of 1,024 threads per
 // filtered row
 // ---------------------------------------------------------------------------
-// A row's threshold is a radix select over order-preserving 32-bit keys of its
-// values (-0 folded into +0), 8 key bits per level: 2 levels for bf16 rows,
-// whose keys carry 16 bits, 4 for fp32.  Top-k counts values per digit; top-p
-// sums their masses exp2((v - M) c) rounded to integer multiples of 2^-40, so
-// that every order of summation gives the same bins.  A row of up to 131,072
-// bf16 or 65,536 fp32 values, 16-byte aligned, is read from HBM once and kept
-// in registers as keys (16 128-bit words per thread, two bf16 keys to a
-// 32-bit lane); every pass after the first runs from there.  Longer or
-// unaligned rows are read again for each pass.
+// A row's threshold is the value of a radix select over order-preserving
+// 32-bit keys of its values (-0 folded into +0), 8 key bits per level: 2
+// levels for bf16 rows, whose keys carry 16 bits, 4 for fp32.  Top-k counts
+// values per digit; top-p sums their masses exp2((v - M) c) rounded to integer
+// multiples of 2^-40, so that every order of summation gives the same totals.
 //
-// The passes are VALU-bound (a wave64 vector instruction takes 4 cycles), so
-// they are lean: the max pass is a packed 16-bit max and min over the keys,
-// the first count level adds every element (-inf and the padding past the row
-// land in digit 0, which is corrected only if the select reaches it), later
-// levels skip every element outside the chosen prefix.  A level's histogram
-// has HCOPY copies, one per lane of a half wave, so lanes of one LDS atomic
-// share an address only when they are 32 apart and agree on the digit; one
-// wave then picks the digit from suffix sums of the merged bins.
+// A row of up to 131,072 bf16 or 65,536 fp32 values, 16-byte aligned, is read
+// from HBM once and kept in registers (16 128-bit words per thread); every
+// later pass runs from there.  Longer or unaligned rows are read again for
+// each pass.  The passes are VALU-bound (a wave64 vector instruction takes 4
+// cycles), so the full-row work is kept to a few instructions per value:
+//
+// * top-k (K <= 1,024): the K-th largest of the 1,024 per-thread maxima is a
+//   lower bound of the K-th largest value; one compare pass appends every
+//   value at or above it to a list in LDS, and the select runs on the list;
+// * top-p without top-k: one pass sums the integer masses per thread in fp64
+//   for the total Z (fp32 sums of the eight values of a 128-bit word, added
+//   in fp64 in a fixed order: deterministic, within about 1e-7), and adds
+//   every term into one of 64 bins by its binary exponent, as its top 13
+//   significant bits (integer LDS atomics, so within 2^-12 of the sum);
+//   the bins below the smallest exponent whose tail, taken 1% heavier,
+//   weighs less than (1 - P) Z cannot hold the cut, so a compare pass against
+//   a value safely below that exponent fills the list, and the select runs on
+//   the list;
+// * top-p after top-k: every value of the top-k set is on the list already.
+//
+// Both selects on a list give the threshold of the full row: every value down
+// to the cut is on the list, so the digit where the sum from the top reaches
+// the goal is the same.  Each wave appends to a segment of its own, its count
+// kept in registers.  A row whose list would overflow a segment, or whose
+// bound is -inf, takes full-row radix passes instead.  A level's histogram has
+// HCOPY copies, one per lane of a half wave, so lanes of one LDS atomic share
+// an address only when they are 32 apart and agree on the digit; one wave then
+// picks the digit from suffix sums of the merged bins.
 constexpr int TW = 1024;          // threads of a threshold workgroup
 constexpr int TNW = TW / 64;
 constexpr int THR_NL = 16;        // 128-bit words per thread of a row kept in registers
 constexpr int HCOPY = 32;         // histogram copies
+constexpr int LIST_BYTES = 65536; // LDS for the candidate keys of a row
+// candidate keys a row may keep: bf16 keys are stored in 16 bits
+template <typename T> constexpr unsigned list_cap() { return LIST_BYTES / (sizeof(T) == 2 ? 2 : 4); }
+constexpr int EBINS = 64;         // exponent bins of the top-p bound
 
 // Keys: the value's bits with the sign bit flipped for non-negative values
 // and every bit flipped for negative ones (unsigned order = value order);
-// bf16 keys are kept in the upper 16 bits of a 32-bit key.
-template <typename T> struct Keys;
-template <> struct Keys<uint16_t> {
-  static constexpr uint32_t NEG = 0x007f0000u;   // key of -inf (also the padding)
-  static constexpr uint32_t POS = 0xff800000u;   // key of +inf
-  // the two keys of a word of two bf16 values, packed
-  static __device__ __forceinline__ uint32_t of_word(uint32_t w) {
-    const uint32_t z = w & 0x7fff7fffu;
-    const uint32_t nz = (z + 0x7fff7fffu) & 0x80008000u;   // magnitude != 0, per half
-    w = (w & nz) | z;                                      // -0 -> +0
-    const uint32_t neg = (w >> 15) & 0x00010001u;
-    return w ^ (neg * 0x7fffu + 0x80008000u);
-  }
-  static __device__ __forceinline__ float value(uint32_t k) {
-    const uint32_t m = (uint32_t)((int32_t)k >> 31) & 0x7fffffffu;
-    return __uint_as_float(~(k ^ m) & 0xffff0000u);
-  }
-};
-template <> struct Keys<float> {
-  static constexpr uint32_t NEG = 0x007fffffu;
-  static constexpr uint32_t POS = 0xff800000u;
-  static __device__ __forceinline__ uint32_t of_word(uint32_t w) {
-    w = (w == 0x80000000u) ? 0u : w;
-    return w ^ ((uint32_t)((int32_t)w >> 31) | 0x80000000u);
-  }
-  static __device__ __forceinline__ float value(uint32_t k) {
-    const uint32_t m = (uint32_t)((int32_t)k >> 31) & 0x7fffffffu;
-    return __uint_as_float(~(k ^ m));
-  }
-};
+// bf16 keys are the upper 16 bits of a 32-bit key, the lower ones zero.
 template <typename T>
-__device__ __forceinline__ uint4 keys_of(uint4 w) {
-  return make_uint4(Keys<T>::of_word(w.x), Keys<T>::of_word(w.y), Keys<T>::of_word(w.z),
-                    Keys<T>::of_word(w.w));
+__device__ __forceinline__ uint32_t vkey(float f) {
+  uint32_t u = __float_as_uint(f);
+  u = (u == 0x80000000u) ? 0u : u;
+  const uint32_t k = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+  return sizeof(T) == 2 ? (k & 0xffff0000u) : k;
 }
+template <typename T>
+__device__ __forceinline__ float keyv(uint32_t k) {
+  const uint32_t m = (uint32_t)((int32_t)k >> 31) & 0x7fffffffu;
+  const uint32_t u = ~(k ^ m);
+  return __uint_as_float(sizeof(T) == 2 ? (u & 0xffff0000u) : u);
+}
+template <typename T> constexpr uint32_t key_neg() { return sizeof(T) == 2 ? 0x007f0000u : 0x007fffffu; }
 
 struct ThrShared {
   union {
     unsigned c[256 * HCOPY];             // [digit][copy] counts
     unsigned long long m[256 * HCOPY];   // [digit][copy] masses (units of 2^-40)
   } h;
+  union {
+    uint32_t k32[LIST_BYTES / 4];
+    uint16_t k16[LIST_BYTES / 2];
+  } list;                                // candidate keys
+  double eb[EBINS];                      // merged exponent bins
+  unsigned wcnt[TNW];                    // list entries appended by each wave
   alignas(16) unsigned long long bins[256];   // merged bins of the level
-  uint32_t kw[2][TNW];
+  float fw[TNW];
   unsigned long long cw[TNW];
+  double dw[TNW];
   double target;                         // top-p: P times the total mass
   unsigned long long above;              // count or mass above the digits chosen so far
-  unsigned long long upper;              // level 0 of top-k: values outside digit 0
+  unsigned long long upper;              // full-row top-k: values outside digit 0
   int digit;
 };
 
@@ -2074,17 +2081,17 @@ __device__ __forceinline__ unsigned long long fixmass(float t) {
   return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
-// f(key) for the keys of one word of keys, in element order.
+// f(v) for the values of one 128-bit word of a row, in element order.
 template <typename T, typename F>
-__device__ __forceinline__ void each_key(const uint4& w, F& f) {
+__device__ __forceinline__ void each_val(const uint4& w, F& f) {
   const uint32_t d[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
     if constexpr (sizeof(T) == 4) {
-      f(d[h]);
+      f(__uint_as_float(d[h]));
     } else {
-      f(d[h] << 16);
-      f(d[h] & 0xffff0000u);
+      f(__uint_as_float(d[h] << 16));
+      f(__uint_as_float(d[h] & 0xffff0000u));
     }
   }
 }
@@ -2107,11 +2114,9 @@ __device__ __forceinline__ uint4 thr_mask(uint4 w, int g, int V) {
   return (e0 + VEC > V) ? mask_tail<T>(w, V - e0, fill_bits<T>(NEG_INF)) : w;
 }
 
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
-// 64-bit DPP moves (two 32-bit moves; lanes without a source read 0) and the
-// wave's inclusive sum in lane order, with no lane-address registers (the
-// level loop would keep those live across every pass)
+// 64-bit DPP moves (two 32-bit moves; lanes without a source read 0), the
+// wave's inclusive sum in lane order and its total, with no lane-address
+// registers (a loop over the levels would keep those live across every pass)
 template <int CTRL, int ROWS = 0xf>
 __device__ __forceinline__ unsigned long long dpp_u64(unsigned long long x) {
   const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, CTRL, ROWS, 0xf, false);
@@ -2133,53 +2138,37 @@ __device__ __forceinline__ unsigned long long readlane_u64(unsigned long long x,
   return ((unsigned long long)hi << 32) | lo;
 }
 
-// Running max and min of the keys of a word of keys (bf16: per 16-bit half).
-template <typename T>
-__device__ __forceinline__ void key_range(const uint4& w, uint32_t& mx, uint32_t& mn) {
-  const uint32_t d[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    if constexpr (sizeof(T) == 4) {
-      mx = max(mx, d[h]);
-      mn = min(mn, d[h]);
-    } else {
-      const u16x2 a = __builtin_bit_cast(u16x2, d[h]);
-      mx = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, mx), a));
-      mn = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, mn), a));
-    }
-  }
-}
-
-__device__ __forceinline__ void thr_block_range(uint32_t& mx, uint32_t& mn, ThrShared& th) {
-  // unsigned order through signed values with the top bit flipped
-  int sx = (int)(mx ^ 0x80000000u), sn = (int)(mn ^ 0x80000000u);
-  sx = wave_reduce_rows(sx, [](int a, int b) { return max(a, b); });
-  sn = wave_reduce_rows(sn, [](int a, int b) { return min(a, b); });
-  mx = (uint32_t)sx ^ 0x80000000u;
-  mn = (uint32_t)sn ^ 0x80000000u;
-  if ((threadIdx.x & 63) == 0) {
-    th.kw[0][threadIdx.x >> 6] = mx;
-    th.kw[1][threadIdx.x >> 6] = mn;
-  }
+__device__ __forceinline__ float thr_block_max(float x, ThrShared& th) {
+  x = wave_reduce_rows(x, [](float a, float b) { return fmax3nan(a, b); });
+  if ((threadIdx.x & 63) == 0) th.fw[threadIdx.x >> 6] = x;
   __syncthreads();
-  mx = th.kw[0][0];
-  mn = th.kw[1][0];
+  float r = th.fw[0];
 #pragma unroll
-  for (int q = 1; q < TNW; ++q) {
-    mx = max(mx, th.kw[0][q]);
-    mn = min(mn, th.kw[1][q]);
-  }
+  for (int q = 1; q < TNW; ++q) r = fmax3nan(r, th.fw[q]);
+  return r;
 }
 
-// Sum of a count over the workgroup (exact in fp64: counts stay below 2^53).
+// Exact sum of a 64-bit count or mass over the workgroup.
 __device__ __forceinline__ unsigned long long thr_block_sum(unsigned long long x, ThrShared& th) {
-  x = (unsigned long long)wave_reduce_rows((double)x, [](double a, double b) { return a + b; });
+  x = readlane_u64(wave_scan_u64(x), 63);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) th.cw[threadIdx.x >> 6] = x;
   __syncthreads();
   unsigned long long r = 0ull;
 #pragma unroll
   for (int q = 0; q < TNW; ++q) r += th.cw[q];
+  return r;
+}
+
+// Sum over the workgroup in a fixed order (deterministic).
+__device__ __forceinline__ double thr_block_sum_d(double x, ThrShared& th) {
+  x = wave_reduce_rows(x, [](double a, double b) { return a + b; });
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) th.dw[threadIdx.x >> 6] = x;
+  __syncthreads();
+  double r = 0.0;
+#pragma unroll
+  for (int q = 0; q < TNW; ++q) r += th.dw[q];
   return r;
 }
 
@@ -2221,9 +2210,11 @@ __device__ __forceinline__ void merge_bins(ThrShared& th) {
 
 // Wave 0 picks the highest digit whose bins from the top, with everything
 // above from earlier levels, reach the goal: K values (counts) or the target
-// mass (masses; at level 0 the target is P times the level's total).
+// mass (masses).  At level 0 the target is P times z, or times the level's
+// total when z < 0.
 template <bool MASS>
-__device__ __forceinline__ void pick_digit(ThrShared& th, int lev, unsigned K, float Pp) {
+__device__ __forceinline__ void pick_digit(ThrShared& th, int lev, unsigned K, float Pp,
+                                           double z = -1.0) {
   const int tid = threadIdx.x;
   if (tid < 64) {
     const int l = tid;
@@ -2235,7 +2226,7 @@ __device__ __forceinline__ void pick_digit(ThrShared& th, int lev, unsigned K, f
     const unsigned long long inc = wave_scan_u64(ls);
     const unsigned long long total = readlane_u64(inc, 63);
     const unsigned long long base = lev == 0 ? 0ull : th.above;
-    const double tgt = lev == 0 ? (double)Pp * (double)total : th.target;
+    const double tgt = lev == 0 ? (double)Pp * (z < 0.0 ? (double)total : z) : th.target;
     unsigned long long c = base + inc - ls;
     int first = 4;
     unsigned long long at = 0ull;
@@ -2262,13 +2253,52 @@ __device__ __forceinline__ void pick_digit(ThrShared& th, int lev, unsigned K, f
   __syncthreads();
 }
 
+// Radix select over the keys of the list: the K-th largest key (MASS false),
+// or the key of the top-p cut of the keys at or above kfloor (MASS true; z the
+// total mass of the set the cut is taken in, or < 0 for the listed keys').
+template <typename T, bool MASS>
+__device__ __forceinline__ uint32_t list_select(ThrShared& th, unsigned K, float Pp, double z,
+                                                uint32_t kfloor, float M, float c) {
+  constexpr int LEVELS = sizeof(T) == 2 ? 2 : 4;
+  const int cp = threadIdx.x & (HCOPY - 1);
+  uint32_t prefix = 0u, pmask = 0u;
+#pragma unroll
+  for (int lev = 0; lev < LEVELS; ++lev) {
+    const int shift = 24 - 8 * lev;
+    clear_bins(th);
+    // each wave walks its own segment of the list
+    const int wv = threadIdx.x >> 6;
+    const unsigned seg = list_cap<T>() / TNW;
+    const unsigned nw = th.wcnt[wv];
+    for (unsigned i = (threadIdx.x & 63); i < nw; i += 64) {
+      const unsigned at = wv * seg + i;
+      const uint32_t k = sizeof(T) == 2 ? (uint32_t)th.list.k16[at] << 16 : th.list.k32[at];
+      if (k >= kfloor && (k & pmask) == prefix) {
+        const uint32_t bin = ((k >> shift) & 255u) * HCOPY + cp;
+        if constexpr (MASS) atomicAdd(&th.h.m[bin], fixmass(term(keyv<T>(k), M, c)));
+        else atomicAdd(&th.h.c[bin], 1u);
+      }
+    }
+    __syncthreads();
+    merge_bins<MASS>(th);
+    pick_digit<MASS>(th, lev, K, Pp, z);
+    prefix |= (uint32_t)th.digit << shift;
+    pmask |= 255u << shift;
+  }
+  return prefix;
+}
+
+// The row's threshold in tau.  The variant that keeps the row in registers
+// (REG) returns false, with nothing written, where a full-row fallback is
+// needed; the caller then runs the variant that reads the row for each pass.
 template <typename T, bool REG>
-__device__ __forceinline__ float row_threshold(const T* __restrict__ rp, int V, bool al,
-                                               const Req& R, ThrShared& th) {
+__device__ __forceinline__ bool row_threshold(const T* __restrict__ rp, int V, bool al,
+                                              const Req& R, ThrShared& th, float& tau) {
   constexpr int VEC = VT<T>::VEC;
   constexpr int LEVELS = sizeof(T) == 2 ? 2 : 4;
-  constexpr uint32_t KNEG = Keys<T>::NEG;
+  constexpr uint32_t KNEG = key_neg<T>();
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const int cp = tid & (HCOPY - 1);
   uint4 w[REG ? THR_NL : 1];
   if constexpr (REG) {
@@ -2282,139 +2312,299 @@ __device__ __forceinline__ float row_threshold(const T* __restrict__ rp, int V, 
     for (int i = 0; i < THR_NL; ++i) {
       const int g0 = i * TW * VEC;
       if (g0 + TW * VEC <= V) w[i] = *reinterpret_cast<const uint4*>(base + g0);
-      else if (g0 < V) w[i] = thr_word<T>(rp, i * TW + tid, V, true);
+      else if (g0 < V) w[i] = thr_mask<T>(thr_word<T>(rp, i * TW + tid, V, true), i * TW + tid, V);
       else w[i] = make_uint4(nw, nw, nw, nw);
     }
-#pragma unroll
-    for (int i = 0; i < THR_NL; ++i) {
-      const int g0 = i * TW * VEC;
-      if (g0 + TW * VEC > V && g0 < V) w[i] = thr_mask<T>(w[i], i * TW + tid, V);
-      w[i] = keys_of<T>(w[i]);
-    }
   }
-  // words(f): f(word of keys) for every word of the thread: from the
-  // registers, or read again eight at a time (padding past the row: -inf)
-  auto words = [&](auto&& f) {
+  // each_read(f): f(v) for every value of the thread (-inf past the row's
+  // end), read from the row eight words at a time
+  auto each_read = [&](auto&& f) {
+    const int ng = (V + VEC - 1) / VEC;
+    for (int g0 = tid; g0 < ng; g0 += 8 * TW) {
+      uint4 q[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = thr_word<T>(rp, min(g0 + i * TW, ng - 1), V, al);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint4 x = thr_mask<T>(q[i], g0 + i * TW, V);
+        if (g0 + i * TW < ng) each_val<T>(x, f);
+      }
+    }
+  };
+  // each(f): the same from the registers when the row is kept there
+  auto each = [&](auto&& f) {
     if constexpr (REG) {
       // the words pass through an empty asm statement first: what a pass
       // derives from them does not depend on the level, and the compiler
-      // would otherwise keep it for every element across the levels
+      // would otherwise keep it for every value across the levels
 #pragma unroll
       for (int i = 0; i < THR_NL; ++i)
         asm volatile("" : "+v"(w[i].x), "+v"(w[i].y), "+v"(w[i].z), "+v"(w[i].w));
 #pragma unroll
-      for (int i = 0; i < THR_NL; ++i) f(w[i]);
+      for (int i = 0; i < THR_NL; ++i) each_val<T>(w[i], f);
     } else {
-      const int ng = (V + VEC - 1) / VEC;
-      for (int g0 = tid; g0 < ng; g0 += 8 * TW) {
-        uint4 q[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = thr_word<T>(rp, min(g0 + i * TW, ng - 1), V, al);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          if (g0 + i * TW < ng) f(keys_of<T>(thr_mask<T>(q[i], g0 + i * TW, V)));
-        }
-      }
+      each_read(f);
     }
   };
-  auto each = [&](auto&& f) { words([&](const uint4& x) { each_key<T>(x, f); }); };
+  // fill_list(vlo): every value at or above vlo goes to the list, each wave's
+  // to its own segment in order; the wave's count stays in a register.
+  // Returns the number of entries, or a number above the capacity when a
+  // segment overflowed.
+  constexpr unsigned SEG = list_cap<T>() / TNW;
+  auto fill_list = [&](float vlo) -> unsigned {
+    const unsigned sbase = (unsigned)(tid >> 6) * SEG;
+    unsigned wc = 0u;
+    each([&](float v) {
+      const bool hit = v >= vlo;
+      const uint64_t m = __ballot(hit);
+      if (m) {
+        const unsigned pos =
+            wc + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (hit && pos < SEG) {
+          if constexpr (sizeof(T) == 2) th.list.k16[sbase + pos] = (uint16_t)(vkey<T>(v) >> 16);
+          else th.list.k32[sbase + pos] = vkey<T>(v);
+        }
+        wc += (unsigned)__popcll(m);
+      }
+    });
+    if (lane == 0) th.wcnt[tid >> 6] = wc;
+    __syncthreads();
+    unsigned n = 0u, big = 0u;
+#pragma unroll
+    for (int q = 0; q < TNW; ++q) {
+      n += th.wcnt[q];
+      big = max(big, th.wcnt[q]);
+    }
+    return big > SEG ? list_cap<T>() + 1u : n;
+  };
 
-  // max and min key: a NaN (keys above +inf's or below -inf's), +inf, or a
-  // row of -inf leaves the row unfiltered (faults are reported by the row pass)
-  uint32_t kmax = 0u, kmin = 0xffffffffu;
-  words([&](const uint4& x) { key_range<T>(x, kmax, kmin); });
-  if constexpr (sizeof(T) == 2) {
-    kmax = max(kmax << 16, kmax & 0xffff0000u);
-    kmin = min(kmin << 16, kmin & 0xffff0000u);
+  // row max and each thread's own max.  A row that holds a NaN or +inf is
+  // reported as a fault by the row pass whatever its threshold, so the max
+  // need not propagate NaN (a plain max is one instruction); +inf or a row of
+  // -inf leaves the row unfiltered.  bf16: the upper value of a word is
+  // compared with the lower one's bits still below it (they perturb it by
+  // less than one bf16 step, so the largest word holds the largest value,
+  // masked once at the end; a word whose upper value is +-inf reads as NaN
+  // and is skipped, harmlessly)
+  float tmax = NEG_INF;
+  {
+    float mh = NEG_INF, ml = NEG_INF;
+    auto wmax = [&](const uint4& q) {
+      const uint32_t d[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        if constexpr (sizeof(T) == 2) {
+          mh = __builtin_fmaxf(mh, __uint_as_float(d[h]));
+          ml = __builtin_fmaxf(ml, __uint_as_float(d[h] << 16));
+        } else {
+          mh = __builtin_fmaxf(mh, __uint_as_float(d[h]));
+        }
+      }
+    };
+    if constexpr (REG) {
+#pragma unroll
+      for (int i = 0; i < THR_NL; ++i) wmax(w[i]);
+    } else {
+      const int ng = (V + VEC - 1) / VEC;
+      for (int g = tid; g < ng; g += TW) wmax(thr_mask<T>(thr_word<T>(rp, g, V, al), g, V));
+    }
+    if constexpr (sizeof(T) == 2) mh = __uint_as_float(__float_as_uint(mh) & 0xffff0000u);
+    tmax = __builtin_fmaxf(mh, ml);
   }
-  thr_block_range(kmax, kmin, th);
-  if (kmax >= Keys<T>::POS || kmin < KNEG || kmax <= KNEG) return NEG_INF;
-  const float M = Keys<T>::value(kmax);
+  const float M = thr_block_max(tmax, th);
+  tau = NEG_INF;
+  if (!(M > NEG_INF && M < POS_INF)) return true;
 
   bool do_k = R.K > 0;
   const bool do_p = R.P > 0.f && R.P < 1.f;
   uint32_t tau_key = 0u;   // keep everything
+  unsigned n_list = 0u;    // valid list entries (0: no list)
   if (do_k) {
     const unsigned K = (unsigned)R.K;
-    uint32_t prefix = 0u, pmask = 0u;
-    unsigned long long ninf = 0ull;   // -inf values and padding (counted only when needed)
+    bool full = true;      // full-row passes
+    if (K <= (unsigned)TW) {
+      // the K-th largest of the threads' maxima: K values are at or above it
+      const uint32_t kt = vkey<T>(tmax);
+      uint32_t prefix = 0u, pmask = 0u;
 #pragma unroll
-    for (int lev = 0; lev < LEVELS; ++lev) {
-      const int shift = 24 - 8 * lev;
-      clear_bins(th);
-      if (lev == 0) {
-        each([&](uint32_t k) { atomicAdd(&th.h.c[(k >> 24) * HCOPY + cp], 1u); });
-      } else {
-        each([&](uint32_t k) {
-          if ((k & pmask) == prefix) atomicAdd(&th.h.c[((k >> shift) & 255u) * HCOPY + cp], 1u);
-        });
-      }
-      __syncthreads();
-      merge_bins<false>(th);
-      if (lev == 0) {
-        // digit 0 holds -inf and the padding: count them only if the select
-        // can reach digit 0 or K may not be below the number of finite values
-        if (tid < 64) {
-          const ulonglong2* bp = reinterpret_cast<const ulonglong2*>(&th.bins[4 * tid]);
-          const ulonglong2 b01 = bp[0], b23 = bp[1];
-          unsigned long long u = (tid ? b01.x : 0ull) + b01.y + b23.x + b23.y;
-          u = (unsigned long long)wave_reduce_rows((double)u, [](double a, double b) { return a + b; });
-          if (tid == 0) th.upper = u;
-        }
+      for (int lev = 0; lev < LEVELS; ++lev) {
+        const int shift = 24 - 8 * lev;
+        clear_bins(th);
+        if ((kt & pmask) == prefix) atomicAdd(&th.h.c[((kt >> shift) & 255u) * HCOPY + cp], 1u);
         __syncthreads();
-        if (th.upper <= (unsigned long long)K) {
-          unsigned long long n = 0ull;
-          each([&](uint32_t k) { n += (k == KNEG) ? 1ull : 0ull; });
-          ninf = thr_block_sum(n, th);
-          const unsigned long long finite = th.upper + th.bins[0] - ninf;
-          if ((unsigned long long)K >= finite) {
+        merge_bins<false>(th);
+        pick_digit<false>(th, lev, K, 0.f);
+        prefix |= (uint32_t)th.digit << shift;
+        pmask |= 255u << shift;
+      }
+      const float lb = keyv<T>(prefix);
+      if (lb > NEG_INF) {
+        const unsigned n = fill_list(lb);
+        if (n <= list_cap<T>()) {
+          full = false;
+          bool keep_all = false;
+          if (n == K) {
+            // exactly K candidates: K is below the number of finite values
+            // only if a finite value lies below the bound
+            unsigned long long below = 0ull;
+            each([&](float v) { below += (v > NEG_INF && v < lb) ? 1ull : 0ull; });
+            keep_all = thr_block_sum(below, th) == 0ull;
+          }
+          if (keep_all) {
             do_k = false;
-            break;
+          } else {
+            tau_key = list_select<T, false>(th, K, 0.f, -1.0, 0u, M, R.c);
+            n_list = n;
           }
         }
       }
-      // -inf values still inside the prefix are not candidates
-      if (tid == 0 && ninf != 0ull && (KNEG & pmask) == prefix) th.bins[(KNEG >> shift) & 255u] -= ninf;
-      __syncthreads();
-      pick_digit<false>(th, lev, K, 0.f);
-      prefix |= (uint32_t)th.digit << shift;
-      pmask |= 255u << shift;
     }
-    if (do_k) tau_key = prefix;
+    if constexpr (REG) {
+      if (full) return false;
+    } else if (full) {
+      uint32_t prefix = 0u, pmask = 0u;
+      unsigned long long ninf = 0ull;   // -inf values and padding (counted only when needed)
+#pragma unroll
+      for (int lev = 0; lev < LEVELS; ++lev) {
+        const int shift = 24 - 8 * lev;
+        clear_bins(th);
+        // -inf and the padding land in digit 0 at level 0
+        each_read([&](float v) {
+          const uint32_t k = vkey<T>(v);
+          if ((k & pmask) == prefix) atomicAdd(&th.h.c[((k >> shift) & 255u) * HCOPY + cp], 1u);
+        });
+        __syncthreads();
+        merge_bins<false>(th);
+        if (lev == 0) {
+          // count -inf only if the select can reach digit 0 or K may not be
+          // below the number of finite values
+          if (tid < 64) {
+            const ulonglong2* bp = reinterpret_cast<const ulonglong2*>(&th.bins[4 * tid]);
+            const ulonglong2 b01 = bp[0], b23 = bp[1];
+            const unsigned long long u = (tid ? b01.x : 0ull) + b01.y + b23.x + b23.y;
+            const unsigned long long tot = readlane_u64(wave_scan_u64(u), 63);
+            if (tid == 0) th.upper = tot;
+          }
+          __syncthreads();
+          if (th.upper <= (unsigned long long)K) {
+            unsigned long long n = 0ull;
+            each_read([&](float v) { n += (v == NEG_INF) ? 1ull : 0ull; });
+            ninf = thr_block_sum(n, th);
+            if ((unsigned long long)K >= th.upper + th.bins[0] - ninf) {
+              do_k = false;
+              break;
+            }
+          }
+        }
+        // -inf values still inside the prefix are not candidates
+        if (tid == 0 && ninf != 0ull && (KNEG & pmask) == prefix) th.bins[(KNEG >> shift) & 255u] -= ninf;
+        __syncthreads();
+        pick_digit<false>(th, lev, K, 0.f);
+        prefix |= (uint32_t)th.digit << shift;
+        pmask |= 255u << shift;
+      }
+      if (do_k) tau_key = prefix;
+    }
   }
   if (do_p) {
-    // the top-k set, -inf excluded (its masses are 0 anyway)
-    const uint32_t kfloor = do_k ? tau_key : KNEG + 1u;
-    uint32_t prefix = 0u, pmask = 0u;
-#pragma unroll
-    for (int lev = 0; lev < LEVELS; ++lev) {
-      const int shift = 24 - 8 * lev;
+    uint32_t pk = 0u;
+    bool full = true;
+    if (do_k && n_list != 0u) {
+      // the top-k set is on the list
+      pk = list_select<T, true>(th, 0u, R.P, -1.0, tau_key, M, R.c);
+      full = false;
+    } else if (!do_k) {
+      // the total mass, exact, and the terms by binary exponent: bin b holds
+      // the terms in [2^-b, 2^(1-b)), the last bin everything below
       clear_bins(th);
-      auto add = [&](uint32_t k) {
-        const unsigned long long fx = fixmass(term(Keys<T>::value(k), M, R.c));
-        atomicAdd(&th.h.m[((k >> shift) & 255u) * HCOPY + cp], fx);
-      };
-      each([&](uint32_t k) {
-        if (k >= kfloor && (k & pmask) == prefix) add(k);
+      double zs = 0.0;
+      float zw = 0.f;
+      int nz = 0;
+      each([&](float v) {
+        const float t = term(v, M, R.c);
+        zw += t;
+        if (++nz == VEC) {   // a word's values (a compile-time count when unrolled)
+          zs += (double)zw;
+          zw = 0.f;
+          nz = 0;
+        }
+        // t = (q + f) 2^-(b+12) with 4,096 <= q < 8,192 and 0 <= f < 1 for
+        // b < 63; the last bin's terms are all below 2^-62
+        const uint32_t tb = __float_as_uint(t);
+        const uint32_t b = min(127u - (tb >> 23), (uint32_t)(EBINS - 1));
+        atomicAdd(&th.h.c[b * HCOPY + cp], 0x1000u | ((tb >> 11) & 0xfffu));
       });
+      zs += (double)zw;
+      const double Zs = thr_block_sum_d(zs, th);
+      const unsigned long long Z = (unsigned long long)(Zs * 1099511627776.0);
+      if (tid < EBINS) {
+        unsigned long long sq = 0ull;
+#pragma unroll
+        for (int q = 0; q < HCOPY; ++q) sq += th.h.c[tid * HCOPY + q];
+        // within 2^-12 below the bin's sum; the last bin is bounded by count
+        th.eb[tid] = tid < EBINS - 1 ? ldexp((double)sq, -(tid + 12)) : ldexp((double)V, -62);
+      }
       __syncthreads();
-      merge_bins<true>(th);
-      pick_digit<true>(th, lev, 0u, R.P);
-      prefix |= (uint32_t)th.digit << shift;
-      pmask |= 255u << shift;
+      // the first exponent whose tail below is light enough (the tails shrink
+      // as the exponent grows, and the last one is empty)
+      if (tid < 64) {
+        double tail = 0.0;
+        for (int b = tid + 1; b < EBINS; ++b) tail += th.eb[b];
+        const bool light = 1.01 * tail * 1099511627776.0 < (1.0 - (double)R.P) * (double)Z;
+        const uint64_t msk = __ballot(tid < EBINS && light);
+        if (tid == 0) th.digit = msk ? (int)__builtin_ctzll(msk) : EBINS - 1;
+      }
+      __syncthreads();
+      // every value whose term reaches 2^-bc is at or above vlo (a factor 2
+      // of margin in the term for the rounding of (v - M) c and of exp2)
+      const int bc = th.digit;
+      const float vlo = __double2float_rd((double)M - (double)(bc + 1) / (double)R.c);
+      if (bc < EBINS - 1 && vlo > NEG_INF) {
+        const unsigned n = fill_list(vlo);
+        if (n <= list_cap<T>()) {
+          pk = list_select<T, true>(th, 0u, R.P, (double)Z, 0u, M, R.c);
+          full = false;
+        }
+      }
     }
-    tau_key = prefix > tau_key ? prefix : tau_key;
+    if constexpr (REG) {
+      if (full) return false;
+    } else if (full) {
+      // the top-k set, -inf excluded (its masses are 0 anyway)
+      const uint32_t kfloor = do_k ? tau_key : KNEG + 1u;
+      uint32_t prefix = 0u, pmask = 0u;
+#pragma unroll
+      for (int lev = 0; lev < LEVELS; ++lev) {
+        const int shift = 24 - 8 * lev;
+        clear_bins(th);
+        each_read([&](float v) {
+          const uint32_t k = vkey<T>(v);
+          if (k >= kfloor && (k & pmask) == prefix)
+            atomicAdd(&th.h.m[((k >> shift) & 255u) * HCOPY + cp], fixmass(term(v, M, R.c)));
+        });
+        __syncthreads();
+        merge_bins<true>(th);
+        pick_digit<true>(th, lev, 0u, R.P);
+        prefix |= (uint32_t)th.digit << shift;
+        pmask |= 255u << shift;
+      }
+      pk = prefix;
+    }
+    tau_key = pk > tau_key ? pk : tau_key;
   }
-  if (!do_k && !do_p) return NEG_INF;
-  return Keys<T>::value(tau_key);
+  tau = (do_k || do_p) ? keyv<T>(tau_key) : NEG_INF;
+  return true;
 }
 
 template <typename T>
 __device__ __forceinline__ float thr_row(const T* __restrict__ rp, int64_t ld, int V, const Req& R,
                                          ThrShared& th) {
   const bool al = (((uintptr_t)rp & 15) == 0) && (((ld * (int64_t)sizeof(T)) & 15) == 0);
-  if (al && V <= THR_NL * TW * VT<T>::VEC) return row_threshold<T, true>(rp, V, true, R, th);
-  return row_threshold<T, false>(rp, V, al, R, th);
+  float tau = NEG_INF;
+  if (al && V <= THR_NL * TW * VT<T>::VEC && row_threshold<T, true>(rp, V, true, R, th, tau)) return tau;
+  __syncthreads();   // the register variant's last LDS reads are done
+  row_threshold<T, false>(rp, V, al, R, th, tau);
+  return tau;
 }
 
 template <typename TT, typename TD, int E>
