@@ -34,6 +34,9 @@ What it computes, and where the pages fix it
   last row) is committed.  Page "FreeToken PR #836", section "Design",
   rejection row and the bullet on argmax drafts (the PR's own verify, equal
   in law to rejection sampling with one-hot drafts).
+* Presence and frequency penalties per verify row, the drafts before a row
+  counted as already generated: page "FreeToken PR #836", section "Design",
+  the bullet on argmax drafts, and its test list (``test_rejection``).
 
 Readings where the pages are silent or disagree (each one is listed in
 DESIGN.md as well):
@@ -56,6 +59,19 @@ DESIGN.md as well):
   Argmax ties go to the lowest index; -0 equals +0.
 * Status codes, first match wins: BAD_K, BAD_PARAM, BAD_TOKEN, NONFINITE,
   EMPTY (see ``verify``).
+* Penalties (the pages name them, not their formula): the usual additive
+  form.  Row j of request b sees the count c(t) = h_b(t) + #{i < j : x_i = t}
+  (h_b: the request's generated-token counts; the drafts x_0..x_{j-1} before
+  the row), and every token with c(t) > 0 gets
+  l'(t) = l(t) - (frequency_b * c(t) + presence_b), evaluated in fp64 and
+  rounded to fp32, then to the logits' storage type (bf16 rows stay bf16
+  values: the logits are processed in their own dtype).  Penalties apply to
+  the target rows of every request, greedy ones included, before the
+  temperature and the filters; draft rows are used as supplied (they are the
+  drafter's distribution).  Non-finite penalties make the request
+  BAD_PARAM.  History entries with a token outside [0, V) or a negative
+  count are ignored, and a request whose history offsets are out of order or
+  out of range has no history.
 
 Parity status of each function
 ------------------------------
@@ -157,6 +173,49 @@ def process(z_raw: np.ndarray, T: float, top_k: int = 0, top_p: float = 1.0) -> 
 # --------------------------------------------------------------------------
 # greedy verify
 # --------------------------------------------------------------------------
+def round_to_dtype(v: np.ndarray, dtype: int) -> np.ndarray:
+    """fp64 values rounded to fp32 (nearest, ties to even), then, for bf16,
+    to bf16 (nearest, ties to even, written out on the fp32 bit pattern);
+    returned as fp64."""
+    with np.errstate(over="ignore"):   # beyond the fp32 range rounds to +-inf
+        f = np.asarray(v, dtype=np.float64).astype(np.float32)
+    if dtype == F32:
+        return f.astype(np.float64)
+    bits = f.view(np.uint32).astype(np.uint64)
+    keep = bits >> np.uint64(16)
+    rest = bits & np.uint64(0xFFFF)
+    up = (rest > 0x8000) | ((rest == 0x8000) & ((keep & np.uint64(1)) == 1))
+    rounded = (keep + up.astype(np.uint64)).astype(np.uint32)
+    nan = np.isnan(f)
+    rounded[nan] = 0x7FC0
+    out = (rounded << np.uint32(16)).view(np.float32).astype(np.float64)
+    return out
+
+
+def penalize(row: np.ndarray, dtype: int, hist_tokens, hist_counts, drafts_before,
+             presence: float, frequency: float) -> np.ndarray:
+    """One verify row's logits after presence / frequency penalties.
+
+    row: the stored values widened to fp64; hist_tokens / hist_counts: the
+    request's generated-token counts; drafts_before: x_0..x_{j-1}.  FreeToken
+    PR #836, section "Design" (the drafts before a row count as generated).
+    """
+    V = row.shape[0]
+    counts: dict[int, int] = {}
+    for t, h in zip(np.asarray(hist_tokens, dtype=np.int64).tolist(),
+                    np.asarray(hist_counts, dtype=np.int64).tolist()):
+        if 0 <= t < V and h >= 0:
+            counts[t] = counts.get(t, 0) + h
+    for x in np.asarray(drafts_before, dtype=np.int64).tolist():
+        counts[x] = counts.get(x, 0) + 1
+    out = row.copy()
+    for t, c in counts.items():
+        if c > 0:
+            d = float(row[t]) - (float(np.float32(frequency)) * c + float(np.float32(presence)))
+            out[t] = round_to_dtype(np.array([d]), dtype)[0]
+    return out
+
+
 def argmax_lowest(row: np.ndarray) -> int:
     """min{y : l_y = max l} on raw values (-0 == +0 under float compare)."""
     m = np.max(row)
@@ -383,9 +442,25 @@ class _ProbRows:
         return widen(self.draft[self.d0 + i, :self.V], self.dtype)
 
 
+def _history(hist_offsets, hist_tokens, hist_counts, b: int):
+    """Request b's (tokens, counts) from the CSR history, empty when its
+    offsets are out of order or out of range."""
+    if hist_offsets is None:
+        return np.zeros(0, np.int64), np.zeros(0, np.int64)
+    off = np.asarray(hist_offsets, dtype=np.int64)
+    nnz = int(np.asarray(hist_tokens).shape[0])
+    h0, h1 = int(off[b]), int(off[b + 1])
+    if not (0 <= h0 <= h1 <= nnz):
+        return np.zeros(0, np.int64), np.zeros(0, np.int64)
+    return (np.asarray(hist_tokens, dtype=np.int64)[h0:h1],
+            np.asarray(hist_counts, dtype=np.int64)[h0:h1])
+
+
 def verify(target, target_dtype, cu_seqlens, draft_tokens, uniforms=None, temperature=None,
            draft=None, draft_dtype=F32, draft_kind=None, top_k=None, top_p=None,
-           vocab=None, max_k=63, greedy_entry=False, keep_cdf=True) -> BatchResult:
+           vocab=None, max_k=63, greedy_entry=False, keep_cdf=True, presence=None,
+           frequency=None, hist_offsets=None, hist_tokens=None,
+           hist_counts=None) -> BatchResult:
     """Whole-batch verify with the boundary's packing.
 
     target:  [total_rows, ld] stored values (uint16 bf16 bits or float32)
@@ -394,9 +469,14 @@ def verify(target, target_dtype, cu_seqlens, draft_tokens, uniforms=None, temper
     cu[b]-b .. cu[b]-b+k_b-1, and uniforms u[cu[b]+i] (i < k_b: acceptance
     draws; i = k_b: the final draw).
 
+    presence, frequency ([batch] or None) and the CSR history
+    (hist_offsets [batch + 1], hist_tokens / hist_counts [nnz]) give the
+    penalties of ``penalize``; a request with both penalties 0 is left alone.
+
     Status per request, first match wins: BAD_K (offsets out of range or
     k_b > max_k), BAD_PARAM (unknown draft kind, a kind that needs draft rows
-    with no draft buffer, or an infinite temperature), BAD_TOKEN (a draft id
+    with no draft buffer, an infinite temperature, or a non-finite penalty),
+    BAD_TOKEN (a draft id
     outside [0, V)), NONFINITE (NaN or +inf in a needed logit row; NaN, inf
     or a negative value in a needed probability), EMPTY (a needed logit row
     with no finite value).  A request with a non-OK status gets accepted = -1,
@@ -428,6 +508,12 @@ def verify(target, target_dtype, cu_seqlens, draft_tokens, uniforms=None, temper
         greedy = greedy_entry or is_greedy_temperature(T)
         kind = None if greedy else int(draft_kind[b])
 
+        a_p = float(np.float32(presence[b])) if presence is not None else 0.0
+        a_f = float(np.float32(frequency[b])) if frequency is not None else 0.0
+        pen = a_p != 0.0 or a_f != 0.0
+        if pen and not (np.isfinite(a_p) and np.isfinite(a_f)):
+            status[b] = ROW_BAD_PARAM
+            continue
         if not greedy and (T == np.inf or kind not in (ONEHOT, LOGITS, PROBS, MATCH)
                            or (kind in (LOGITS, PROBS) and draft is None)):
             status[b] = ROW_BAD_PARAM
@@ -438,6 +524,10 @@ def verify(target, target_dtype, cu_seqlens, draft_tokens, uniforms=None, temper
             continue
 
         rows = [widen(target[c0 + j, :V], target_dtype) for j in range(k + 1)]
+        if pen:
+            ht, hc = _history(hist_offsets, hist_tokens, hist_counts, b)
+            rows = [penalize(rows[j], target_dtype, ht, hc, xs[:j], a_p, a_f)
+                    for j in range(k + 1)]
         drows = None
         if kind == LOGITS:
             drows = [widen(np.asarray(draft)[d0 + j, :V], draft_dtype) for j in range(k)]
@@ -664,4 +754,5 @@ __all__ = [
     "accept_scan", "final_weights", "inverse_cdf", "final_draw", "sampled_request",
     "SampledRecord", "verify", "BatchResult", "request_bounds", "is_greedy_temperature",
     "expected_tokens_per_step", "acceptance_rate", "excusal", "drain", "accounting",
+    "penalize", "round_to_dtype",
 ]
