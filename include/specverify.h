@@ -204,6 +204,48 @@ int spec_verify_sampled(const void* target_logits, int target_dtype, int64_t ld_
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * spec_verify_sampled with presence and frequency penalties applied per verify
+ * row, the drafts before a row counted as already generated ("FreeToken PR
+ * #836", section "Design", the bullet on argmax drafts).  Row j of request b
+ * counts c(t) = h_b(t) + #{i < j : x_i = t}; every token with c(t) > 0 gets
+ *   l'(t) = l(t) - (frequency[b] * c(t) + presence[b])
+ * evaluated in fp64 and rounded to fp32, then to target_dtype (nearest, ties
+ * to even), before temperature, top-k and top-p.  Penalties apply to the
+ * target rows of every request, greedy ones included; draft rows are used as
+ * supplied.  A request with both penalties 0 is verified exactly as by
+ * spec_verify_sampled; a non-finite penalty makes it SV_ROW_BAD_PARAM.
+ *   presence, frequency  float [batch], device.
+ *   hist_offsets   int32 [batch + 1] or NULL (no history); request b's
+ *                  generated-token counts are entries
+ *                  [hist_offsets[b], hist_offsets[b+1]) of
+ *   hist_tokens, hist_counts  int32 [hist_nnz]: token ids (unique within a
+ *                  request) and counts.  Entries with a token outside
+ *                  [0, vocab) or a negative count are ignored; offsets out of
+ *                  order or outside [0, hist_nnz] give the request no history.
+ *   penalized_target  device buffer of total_rows * ld_target elements of
+ *                  target_dtype, written by the call (the penalized rows of
+ *                  the requests with a nonzero penalty; other rows are left
+ *                  as they were) and read by it; it must not alias the inputs.
+ *   Other arguments, layouts and outputs: as spec_verify_sampled.  Returns as
+ *   spec_verify_sampled, and SV_ERR_NULL for a NULL presence, frequency or
+ *   penalized_target (or history arrays with hist_nnz > 0), SV_ERR_SHAPE for
+ *   hist_nnz outside [0, 2^31).
+ */
+int spec_verify_sampled_penalized(const void* target_logits, int target_dtype, int64_t ld_target,
+                                  const void* draft, int draft_dtype, int64_t ld_draft,
+                                  const int32_t* draft_kind, const int32_t* cu_seqlens,
+                                  const int32_t* draft_tokens, const float* uniforms,
+                                  const float* temperature, const int32_t* top_k,
+                                  const float* top_p, const float* presence,
+                                  const float* frequency, const int32_t* hist_offsets,
+                                  const int32_t* hist_tokens, const int32_t* hist_counts,
+                                  int64_t hist_nnz, void* penalized_target, int batch,
+                                  int total_rows, int max_k, int vocab, int32_t* accepted,
+                                  int32_t* out_tokens, float* p_at_draft, float* q_at_draft,
+                                  int32_t* status, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/*
  * Drain of a verified batch ("FreeToken PR #836", section "Design", drain row:
  * commit n = accepted + 1 tokens and give back the unused slots; "Adding
  * Speculative Decoding", "The four high-risk coupling points" item 1: accept

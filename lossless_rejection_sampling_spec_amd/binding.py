@@ -63,6 +63,11 @@ def load_library(path: str) -> ctypes.CDLL:
     L.spec_verify_accounting.restype = _i32
     L.spec_verify_accounting.argtypes = [_vp, _vp, _vp, _i32, _vp, _vp, ctypes.c_float,
                                          ctypes.c_float, _i32, _i32, _vp, _vp, _vp]
+    L.spec_verify_sampled_penalized.restype = _i32
+    L.spec_verify_sampled_penalized.argtypes = [
+        _vp, _i32, _i64, _vp, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+        _vp, _vp, _vp, _vp, _vp, _i64, _vp,
+        _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
     L.spec_verify_sampled_noalloc.restype = _i32
     L.spec_verify_sampled_noalloc.argtypes = [
         _vp, _i32, _i64, _vp, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -198,8 +203,15 @@ def verify_sampled(target: torch.Tensor, draft: torch.Tensor | None, draft_kind:
                    temperature: torch.Tensor, top_k: torch.Tensor | None = None,
                    top_p: torch.Tensor | None = None, *, max_k: int, vocab: int | None = None,
                    want_probs: bool = False, workspace: torch.Tensor | None = None,
-                   out: tuple | None = None):
+                   out: tuple | None = None, presence: torch.Tensor | None = None,
+                   frequency: torch.Tensor | None = None, history: tuple | None = None,
+                   penalized: torch.Tensor | None = None):
     """Sampled verify by rejection sampling (greedy requests mixed in).
+
+    With presence and frequency (float32 [B]) the call goes to
+    spec_verify_sampled_penalized: history = (offsets int32 [B+1], tokens
+    int32 [nnz], counts int32 [nnz]) or None, and `penalized` the scratch of
+    the penalized rows (allocated like `target` when None).
 
     Returns (accepted[B], out_tokens[R], status[B], p_at_draft, q_at_draft);
     the last two are None unless want_probs."""
@@ -230,14 +242,42 @@ def verify_sampled(target: torch.Tensor, draft: torch.Tensor | None, draft_kind:
     if need == 0:
         raise ValueError("invalid sizes for spec_verify_sampled")
     ws = get_workspace(dev, need) if workspace is None else workspace
-    rc = lib().spec_verify_sampled(
-        _ptr(target), _dtype_code(target), target.stride(0),
-        _ptr(draft), _dtype_code(draft) if draft is not None else SV_F32,
-        draft.stride(0) if draft is not None else 0,
-        _ptr(draft_kind), _ptr(cu_seqlens), _ptr(draft_tokens) if n_draft else None,
-        _ptr(uniforms), _ptr(temperature), _ptr(top_k), _ptr(top_p),
-        batch, total_rows, max_k, V, _ptr(accepted), _ptr(tokens), _ptr(p_at), _ptr(q_at),
-        _ptr(status), _ptr(ws), ws.numel(), _stream(dev))
+    if presence is None and frequency is None:
+        rc = lib().spec_verify_sampled(
+            _ptr(target), _dtype_code(target), target.stride(0),
+            _ptr(draft), _dtype_code(draft) if draft is not None else SV_F32,
+            draft.stride(0) if draft is not None else 0,
+            _ptr(draft_kind), _ptr(cu_seqlens), _ptr(draft_tokens) if n_draft else None,
+            _ptr(uniforms), _ptr(temperature), _ptr(top_k), _ptr(top_p),
+            batch, total_rows, max_k, V, _ptr(accepted), _ptr(tokens), _ptr(p_at), _ptr(q_at),
+            _ptr(status), _ptr(ws), ws.numel(), _stream(dev))
+    else:
+        _check_vec(presence, "presence", torch.float32, batch)
+        _check_vec(frequency, "frequency", torch.float32, batch)
+        h_off = h_tok = h_cnt = None
+        nnz = 0
+        if history is not None:
+            h_off, h_tok, h_cnt = history
+            nnz = h_tok.numel()
+            _check_vec(h_off, "history offsets", torch.int32, batch + 1)
+            _check_vec(h_tok, "history tokens", torch.int32, nnz)
+            _check_vec(h_cnt, "history counts", torch.int32, nnz)
+        if penalized is None:
+            penalized = torch.empty_strided(target.shape, target.stride(), dtype=target.dtype,
+                                            device=dev)
+        if (penalized.dtype != target.dtype or penalized.stride() != target.stride()
+                or penalized.shape != target.shape or penalized.device != dev):
+            raise ValueError("penalized must match target's shape, strides, dtype and device")
+        rc = lib().spec_verify_sampled_penalized(
+            _ptr(target), _dtype_code(target), target.stride(0),
+            _ptr(draft), _dtype_code(draft) if draft is not None else SV_F32,
+            draft.stride(0) if draft is not None else 0,
+            _ptr(draft_kind), _ptr(cu_seqlens), _ptr(draft_tokens) if n_draft else None,
+            _ptr(uniforms), _ptr(temperature), _ptr(top_k), _ptr(top_p),
+            _ptr(presence), _ptr(frequency), _ptr(h_off) if nnz else None,
+            _ptr(h_tok) if nnz else None, _ptr(h_cnt) if nnz else None, nnz, _ptr(penalized),
+            batch, total_rows, max_k, V, _ptr(accepted), _ptr(tokens), _ptr(p_at), _ptr(q_at),
+            _ptr(status), _ptr(ws), ws.numel(), _stream(dev))
     _raise(rc)
     return accepted, tokens, status, p_at, q_at
 

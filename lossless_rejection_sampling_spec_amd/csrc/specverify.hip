@@ -138,6 +138,16 @@ struct Params {
   u64* thr_d;
   u64* pq;        // [batch][2 * max_k] p(x_i), q(x_i) handed to the last helper of a request
   u64* ctl;       // [0]: nonzero once a wait ran out (the workspace is poisoned)
+  // penalties (the penalized entry point; pen == nullptr otherwise): the
+  // target rows of a request with a nonzero penalty are read from pen, a
+  // copy with the same pitch in which k_penalize has penalized them
+  const void* pen;
+  const float* pres;
+  const float* freq;
+  const int32_t* hist_off;   // [batch + 1] CSR offsets of the generated-token counts
+  const int32_t* hist_tok;   // [hist_nnz] token ids
+  const int32_t* hist_cnt;   // [hist_nnz] counts
+  int64_t hist_nnz;
   int64_t ld_t, ld_d;
   int batch, total_rows, max_k, vocab, nc;
   int S;          // chunks per producer strip
@@ -375,7 +385,18 @@ struct Req {
   bool filt;
   float c;    // log2(e) / T rounded to fp32
   double ce;  // the same value in fp64
+  bool pen;   // nonzero penalties: the target rows come from the penalized copy
 };
+
+// Whether request b has nonzero penalties (only the penalized entry point
+// passes them).
+__device__ __forceinline__ bool pen_of(const Params& P, int b) {
+  return P.pen != nullptr && (ldu(P.pres + b) != 0.f || ldu(P.freq + b) != 0.f);
+}
+template <typename TT>
+__device__ __forceinline__ const TT* target_rows(const Params& P, bool pen) {
+  return (const TT*)(pen ? P.pen : P.target);
+}
 
 __device__ __forceinline__ Req load_req(const Params& P, int b) {
   Req R;
@@ -388,9 +409,14 @@ __device__ __forceinline__ Req load_req(const Params& P, int b) {
   R.T = T;
   R.greedy = P.greedy_entry || !(R.T >= FLT_MIN);
   R.kind = R.greedy ? -1 : kind;
-  R.bad_param = !R.greedy &&
-                (R.T == POS_INF || R.kind < SV_DRAFT_ONEHOT || R.kind > SV_DRAFT_MATCH ||
-                 ((R.kind == SV_DRAFT_LOGITS || R.kind == SV_DRAFT_PROBS) && P.draft == nullptr));
+  const float ap = P.pen ? ldu(P.pres + b) : 0.f;
+  const float af = P.pen ? ldu(P.freq + b) : 0.f;
+  R.pen = ap != 0.f || af != 0.f;
+  const bool pen_bad = R.pen && !(__builtin_isfinite(ap) && __builtin_isfinite(af));
+  R.bad_param = pen_bad ||
+                (!R.greedy &&
+                 (R.T == POS_INF || R.kind < SV_DRAFT_ONEHOT || R.kind > SV_DRAFT_MATCH ||
+                  ((R.kind == SV_DRAFT_LOGITS || R.kind == SV_DRAFT_PROBS) && P.draft == nullptr)));
   R.K = R.greedy ? 0 : K;
   R.P = R.greedy ? 1.f : Pp;
   if (R.K >= P.vocab) R.K = 0;
@@ -840,7 +866,7 @@ __device__ __forceinline__ void produce(const Params& P, const Req& R, int b, in
   const int nc = P.nc;
   const int row = cu0 + j;
   const int d0 = cu0 - b;
-  const TT* trow = (const TT*)P.target + (int64_t)row * P.ld_t;
+  const TT* trow = target_rows<TT>(P, R.pen) + (int64_t)row * P.ld_t;
   // the draft id and the thresholds are loaded without waiting for the
   // request's parameters, which only decide whether they are used
   const int xr = j < k ? ldu(P.drafts + d0 + j) : -1;
@@ -1111,7 +1137,7 @@ __device__ __forceinline__ int draw_target_row(const Params& P, const Req& R, in
   const double tl = ds.tl / rc(ch);
   const int c0 = ch * CHUNK;
   const int n = min(CHUNK, P.vocab - c0);
-  const TT* rp = (const TT*)P.target + (int64_t)row * P.ld_t;
+  const TT* rp = target_rows<TT>(P, R.pen) + (int64_t)row * P.ld_t;
   const bool vec_ok = AL;
   const float cf = R.c;
   auto wf = [=](float x, float, int e) -> double {
@@ -1588,7 +1614,7 @@ __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, i
   }
   const int trow = cu0 + a;
   const int drow = cu0 - b + a;
-  const TT* tp = (const TT*)P.target + (int64_t)trow * P.ld_t;
+  const TT* tp = target_rows<TT>(P, R.pen) + (int64_t)trow * P.ld_t;
   const TD* dp = (const TD*)P.draft + (int64_t)drow * P.ld_d;
   const bool tvec = AL;
   const bool dvec = AL;
@@ -1978,8 +2004,8 @@ __global__ __launch_bounds__(WG, 4) void k_verify(const Params P) {
   if (j > k) return;
   // the strip's first chunk is requested before the request's parameters
   Buf<TT, TD> A;
-  issue_task<TT, TD, AL>((const TT*)P.target + (int64_t)(cu0 + j) * P.ld_t, (const TD*)nullptr,
-                         false, s * P.S, P.vocab, A);
+  issue_task<TT, TD, AL>(target_rows<TT>(P, pen_of(P, b)) + (int64_t)(cu0 + j) * P.ld_t,
+                         (const TD*)nullptr, false, s * P.S, P.vocab, A);
   const Req R = load_req(P, b);
   if (!R.bad_param) produce<TT, TD, AL>(P, R, b, cu0, k, j, s, ps, A);
   if (j == k && s == P.ns - 1) finalize<TT, TD, AL>(P, b, cu0, k, R, sm, fs, ds, stage);
@@ -2627,15 +2653,99 @@ __global__ __launch_bounds__(TW) void k_thresh(const Params P) {
   u64* out = side == 0 ? P.thr_t + cu0 + j : P.thr_d + (cu0 - b + j);
   float tau;
   if constexpr (std::is_same<TT, TD>::value) {   // one copy of the code for both sides
-    const TT* rp = side == 0 ? (const TT*)P.target + (int64_t)(cu0 + j) * P.ld_t
+    const TT* rp = side == 0 ? target_rows<TT>(P, R.pen) + (int64_t)(cu0 + j) * P.ld_t
                              : (const TT*)P.draft + (int64_t)(cu0 - b + j) * P.ld_d;
     tau = thr_row<TT>(rp, side == 0 ? P.ld_t : P.ld_d, P.vocab, R, th);
   } else if (side == 0) {
-    tau = thr_row<TT>((const TT*)P.target + (int64_t)(cu0 + j) * P.ld_t, P.ld_t, P.vocab, R, th);
+    tau = thr_row<TT>(target_rows<TT>(P, R.pen) + (int64_t)(cu0 + j) * P.ld_t, P.ld_t, P.vocab,
+                      R, th);
   } else {
     tau = thr_row<TD>((const TD*)P.draft + (int64_t)(cu0 - b + j) * P.ld_d, P.ld_d, P.vocab, R, th);
   }
   if (threadIdx.x == 0) *out = (u64)__float_as_uint(tau);
+}
+
+// ---------------------------------------------------------------------------
+// k_penalize: presence / frequency penalties (the penalized entry point)
+// ---------------------------------------------------------------------------
+// One workgroup per verify row j of a request with a nonzero penalty: the row
+// is copied to the same place in P.pen, then every token t the row counts
+// as generated (c(t) = history count + occurrences among the drafts x_0 ..
+// x_{j-1}, c > 0) gets l(t) - (frequency c + presence), evaluated in fp64 and
+// rounded to fp32, then to the logits' type (nearest, ties to even).  Each
+// such token is written once: a history entry counts the drafts equal to its
+// token and marks them; a draft not marked is written by its first occurrence.
+__device__ __forceinline__ void store_pen(float* row, int t, double v) {
+  row[t] = __double2float_rn(v);
+}
+__device__ __forceinline__ void store_pen(uint16_t* row, int t, double v) {
+  const float f = __double2float_rn(v);
+  uint32_t u = __float_as_uint(f);
+  u = (f != f) ? 0x7fc00000u : u + 0x7fffu + ((u >> 16) & 1u);
+  row[t] = (uint16_t)(u >> 16);
+}
+
+template <typename TT, int E>
+__global__ __launch_bounds__(WG) void k_penalize(const Params P) {
+  __shared__ int xs[MAX_K + 1];
+  __shared__ int marked[MAX_K + 1];
+  const int tid = threadIdx.x;
+  const int j = blockIdx.x % (P.max_k + 1);
+  const int b = blockIdx.x / (P.max_k + 1);
+  const int cu0 = ldu(P.cu + b), cu1 = ldu(P.cu + b + 1);
+  const int k = cu1 - cu0 - 1;
+  const float ap = ldu(P.pres + b), af = ldu(P.freq + b);
+  if (j > k || !(ap != 0.f || af != 0.f) || !(__builtin_isfinite(ap) && __builtin_isfinite(af)))
+    return;
+  if (!offsets_ok<E>(P, b, cu0, cu1)) return;   // the verdict k_verify gives
+  const int V = P.vocab;
+  const int row = cu0 + j;
+  const TT* src = (const TT*)P.target + (int64_t)row * P.ld_t;
+  TT* dst = (TT*)const_cast<void*>(P.pen) + (int64_t)row * P.ld_t;
+  constexpr int VEC = VT<TT>::VEC;
+  const bool al = ((((uintptr_t)src) | ((uintptr_t)dst)) & 15) == 0;
+  int e = 0;
+  if (al) {
+    for (e = tid * VEC; e + VEC <= V; e += WG * VEC)
+      *reinterpret_cast<uint4*>(dst + e) = *reinterpret_cast<const uint4*>(src + e);
+    e = (V / VEC) * VEC + tid;
+  } else {
+    e = tid;
+  }
+  for (; e < V; e += WG) dst[e] = src[e];
+  const int d0 = cu0 - b;
+  if (tid < j) {
+    xs[tid] = P.drafts[d0 + tid];
+    marked[tid] = 0;
+  }
+  __syncthreads();   // the copy's stores land before the updates below
+  const double fa = (double)af, pa = (double)ap;
+  int h0 = P.hist_off ? P.hist_off[b] : 0, h1 = P.hist_off ? P.hist_off[b + 1] : 0;
+  if (!(0 <= h0 && h0 <= h1 && (int64_t)h1 <= P.hist_nnz)) h0 = h1 = 0;
+  for (int h = h0 + tid; h < h1; h += WG) {
+    const int t = P.hist_tok[h];
+    const int n = P.hist_cnt[h];
+    if (t < 0 || t >= V || n < 0) continue;
+    int c = n;
+    for (int i = 0; i < j; ++i) {
+      if (xs[i] == t) {
+        ++c;
+        marked[i] = 1;
+      }
+    }
+    if (c > 0) store_pen(dst, t, (double)to_f(src[t]) - (fa * (double)c + pa));
+  }
+  __syncthreads();
+  if (tid < j) {
+    const int t = xs[tid];
+    bool first = t >= 0 && t < V && !marked[tid];
+    for (int i = 0; i < tid; ++i) first = first && xs[i] != t;
+    if (first) {
+      int c = 0;
+      for (int i = 0; i < j; ++i) c += xs[i] == t ? 1 : 0;
+      store_pen(dst, t, (double)to_f(src[t]) - (fa * (double)c + pa));
+    }
+  }
 }
 
 __global__ void k_fill_zero(uint4* p, size_t n16, unsigned char* tail, size_t ntail) {
@@ -2694,6 +2804,13 @@ static int launch_all(Params P, bool sampled, bool filters, bool aligned, hipStr
   const size_t lds = (size_t)8 * (2 * P.max_k + 1) * P.nc;
   // requests per lane when finding a request by launch position or checking
   // its offsets
+  if (P.pen) {
+    const long long gp = (long long)P.batch * (P.max_k + 1);
+    if (P.batch <= 64)
+      hipLaunchKernelGGL((k_penalize<TT, 1>), dim3((unsigned)gp), dim3(WG), 0, st, P);
+    else
+      hipLaunchKernelGGL((k_penalize<TT, 16>), dim3((unsigned)gp), dim3(WG), 0, st, P);
+  }
   if (filters) {
     const long long g0 = (long long)P.batch * (P.max_k + 1) * 2;
     if (P.batch <= 64)
@@ -2724,6 +2841,7 @@ static bool rows_aligned(const void* base, int64_t ld, int elem) {
 static int dispatch(const Params& P, int tdt, int ddt, bool sampled, bool filters,
                     hipStream_t st) {
   const bool al = rows_aligned(P.target, P.ld_t, tdt == SV_F32 ? 4 : 2) &&
+                  rows_aligned(P.pen, P.ld_t, tdt == SV_F32 ? 4 : 2) &&
                   rows_aligned(P.draft, P.ld_d, ddt == SV_F32 ? 4 : 2);
   if (tdt == SV_F32 && ddt == SV_F32)
     return launch_all<float, float>(P, sampled, filters, al, st);
@@ -2794,6 +2912,17 @@ static int fill_zero(void* p, size_t nbytes, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }
 
+// The penalty inputs of the penalized entry point.
+struct Penalties {
+  const float* presence;
+  const float* frequency;
+  const int32_t* hist_offsets;
+  const int32_t* hist_tokens;
+  const int32_t* hist_counts;
+  int64_t hist_nnz;
+  void* penalized;
+};
+
 // The sampled verify with a caller's workspace, or (noalloc) with the
 // current device's scratch array, cleared first over the bytes it needs.
 static int sampled_call(const void* target_logits, int target_dtype, int64_t ld_target,
@@ -2804,10 +2933,16 @@ static int sampled_call(const void* target_logits, int target_dtype, int64_t ld_
                         int batch, int total_rows, int max_k, int vocab, int32_t* accepted,
                         int32_t* out_tokens, float* p_at_draft, float* q_at_draft,
                         int32_t* status, void* workspace, size_t workspace_bytes, bool noalloc,
-                        void* stream) {
+                        void* stream, const Penalties* pen = nullptr) {
   if (!target_logits || !draft_kind || !cu_seqlens || !uniforms || !temperature || !accepted ||
       !out_tokens || !status)
     return SV_ERR_NULL;
+  if (pen) {
+    if (!pen->presence || !pen->frequency || !pen->penalized) return SV_ERR_NULL;
+    if (pen->hist_nnz < 0 || pen->hist_nnz > INT32_MAX) return SV_ERR_SHAPE;
+    if (pen->hist_nnz > 0 && (!pen->hist_offsets || !pen->hist_tokens || !pen->hist_counts))
+      return SV_ERR_NULL;
+  }
   if (!draft_tokens && total_rows > batch) return SV_ERR_NULL;
   if (target_dtype != SV_F32 && target_dtype != SV_BF16) return SV_ERR_DTYPE;
   if (draft && draft_dtype != SV_F32 && draft_dtype != SV_BF16) return SV_ERR_DTYPE;
@@ -2848,6 +2983,15 @@ static int sampled_call(const void* target_logits, int target_dtype, int64_t ld_
   P.vocab = vocab;
   P.nc = nc;
   P.greedy_entry = 0;
+  if (pen) {
+    P.pen = pen->penalized;
+    P.pres = pen->presence;
+    P.freq = pen->frequency;
+    P.hist_off = pen->hist_nnz > 0 ? pen->hist_offsets : nullptr;
+    P.hist_tok = pen->hist_tokens;
+    P.hist_cnt = pen->hist_counts;
+    P.hist_nnz = pen->hist_nnz;
+  }
   carve(P, workspace, L);
   const bool filters = top_k != nullptr || top_p != nullptr;
   if (!filters) {
@@ -2949,6 +3093,28 @@ int spec_verify_sampled(const void* target_logits, int target_dtype, int64_t ld_
                       draft_kind, cu_seqlens, draft_tokens, uniforms, temperature, top_k, top_p,
                       batch, total_rows, max_k, vocab, accepted, out_tokens, p_at_draft,
                       q_at_draft, status, workspace, workspace_bytes, false, stream);
+}
+
+int spec_verify_sampled_penalized(const void* target_logits, int target_dtype, int64_t ld_target,
+                                  const void* draft, int draft_dtype, int64_t ld_draft,
+                                  const int32_t* draft_kind, const int32_t* cu_seqlens,
+                                  const int32_t* draft_tokens, const float* uniforms,
+                                  const float* temperature, const int32_t* top_k,
+                                  const float* top_p, const float* presence,
+                                  const float* frequency, const int32_t* hist_offsets,
+                                  const int32_t* hist_tokens, const int32_t* hist_counts,
+                                  int64_t hist_nnz, void* penalized_target, int batch,
+                                  int total_rows, int max_k, int vocab, int32_t* accepted,
+                                  int32_t* out_tokens, float* p_at_draft, float* q_at_draft,
+                                  int32_t* status, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  if (!workspace) return SV_ERR_NULL;
+  const Penalties pen = {presence, frequency, hist_offsets, hist_tokens, hist_counts, hist_nnz,
+                         penalized_target};
+  return sampled_call(target_logits, target_dtype, ld_target, draft, draft_dtype, ld_draft,
+                      draft_kind, cu_seqlens, draft_tokens, uniforms, temperature, top_k, top_p,
+                      batch, total_rows, max_k, vocab, accepted, out_tokens, p_at_draft,
+                      q_at_draft, status, workspace, workspace_bytes, false, stream, &pen);
 }
 
 int spec_verify_sampled_noalloc(const void* target_logits, int target_dtype, int64_t ld_target,

@@ -308,3 +308,46 @@ def algorithmic_bytes(w: Workload, accepted: np.ndarray | None = None) -> int:
                 total += w.vocab * dsz
     total += 12 * w.total_rows + 24 * w.batch
     return int(total)
+
+
+@dataclass
+class PenaltyInputs:
+    """Presence / frequency penalties of a batch and its generated-token
+    counts (CSR: request b owns entries offsets[b]..offsets[b+1])."""
+    presence: np.ndarray      # float32 [batch]
+    frequency: np.ndarray     # float32 [batch]
+    offsets: np.ndarray       # int32 [batch + 1]
+    tokens: np.ndarray        # int32 [nnz], unique within a request
+    counts: np.ndarray        # int32 [nnz]
+
+
+def penalties(w: Workload, seed: int = 0, share: float = 0.75, hist_len=(0, 200),
+              max_count: int = 5, from_drafts: float = 0.3) -> PenaltyInputs:
+    """Seeded penalty inputs for workload w: a `share` of the requests get
+    nonzero penalties (multiples of 1/16 in [-0.5, 2], exact in bf16 and fp32);
+    each request's history holds a random number of distinct tokens in
+    `hist_len`, some of them (`from_drafts`) taken from its own drafts, with
+    counts in [0, max_count]."""
+    rng = np.random.default_rng([seed, w.config, 77])
+    B, V = w.batch, w.vocab
+    on = rng.random(B) < share
+    grid = np.arange(-8, 33) / 16.0
+    presence = np.where(on, rng.choice(grid, size=B), 0.0).astype(np.float32)
+    frequency = np.where(on, rng.choice(grid, size=B), 0.0).astype(np.float32)
+    cu = w.cu_seqlens
+    offsets = np.zeros(B + 1, dtype=np.int32)
+    toks, cnts = [], []
+    for b in range(B):
+        n = int(rng.integers(hist_len[0], hist_len[1] + 1))
+        d0, k = int(cu[b]) - b, int(cu[b + 1] - cu[b] - 1)
+        own = np.asarray(w.draft_tokens[d0:d0 + k], dtype=np.int64)
+        pick = own[rng.random(own.shape[0]) < from_drafts] if own.size else own
+        rest = rng.choice(V, size=min(n, V), replace=False)
+        t = np.unique(np.concatenate([pick, rest]).astype(np.int64))[:max(n, pick.size)]
+        t = rng.permutation(t)
+        toks.append(t)
+        cnts.append(rng.integers(0, max_count + 1, size=t.size))
+        offsets[b + 1] = offsets[b] + t.size
+    return PenaltyInputs(presence, frequency, offsets,
+                         np.concatenate(toks).astype(np.int32) if toks else np.zeros(0, np.int32),
+                         np.concatenate(cnts).astype(np.int32) if cnts else np.zeros(0, np.int32))

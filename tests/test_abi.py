@@ -23,7 +23,8 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("spec_verify_greedy", "spec_verify_sampled", "spec_verify_workspace_bytes",
               "spec_verify_workspace_init", "spec_verify_abi_version",
-              "spec_verify_status_string"):
+              "spec_verify_status_string", "spec_verify_sampled_penalized",
+              "spec_verify_sampled_noalloc", "spec_verify_drain", "spec_verify_accounting"):
         assert n in names
 
 
@@ -116,6 +117,25 @@ def test_noalloc_rejects_before_any_device_call():
                                          None) == 1
 
 
+def test_penalized_validation():
+    """The penalized entry point checks its extra pointers and sizes on the host."""
+    L = binding.lib()
+    f = FAKE
+
+    def call(pres=f, freq=f, off=None, tok=None, cnt=None, nnz=0, pen=f, ws=f):
+        return L.spec_verify_sampled_penalized(
+            f, 1, 100, None, 0, 0, f, f, f, f, f, None, None, pres, freq, off, tok, cnt, nnz,
+            pen, 2, 6, 3, 100, f, f, None, None, f, ws, 1 << 20, None)
+
+    assert call(pres=None) == 1
+    assert call(freq=None) == 1
+    assert call(pen=None) == 1
+    assert call(ws=None) == 1
+    assert call(nnz=5) == 1               # history arrays missing
+    assert call(nnz=-1) == 2
+    assert call(off=f, tok=f, cnt=f, nnz=1 << 31) == 2
+
+
 def test_drain_and_accounting_validation():
     L = binding.lib()
     f = FAKE
@@ -143,7 +163,8 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
 
 def test_ctypes_signatures_match_header_arity():
     src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
-    for name in ("spec_verify_greedy", "spec_verify_sampled", "spec_verify_sampled_noalloc"):
+    for name in ("spec_verify_greedy", "spec_verify_sampled", "spec_verify_sampled_noalloc",
+                 "spec_verify_sampled_penalized", "spec_verify_drain", "spec_verify_accounting"):
         m = re.search(name + r"\s*\(([^;]*)\);", src, flags=re.S)
         n_args = len([a for a in m.group(1).split(",") if a.strip()])
         assert len(getattr(binding.lib(), name).argtypes) == n_args, name
