@@ -766,9 +766,16 @@ __device__ __forceinline__ CStat chunk_stats(Seg<T>& sg, bool greedy, float tau,
       }
     }
   };
-  if (own) {
-    if (fast) sum_terms([&](float v) { return fterm(v, c, mc); });
-    else sum_terms([&](float v) { return term(v, m, c); });
+  // the one-FMA loop always runs (a per-thread choice between the two loops
+  // slowed the common case); a wave with a thread beyond 2^30 redoes that
+  // thread's terms afterwards, on a wave-uniform branch
+  if (own) sum_terms([&](float v) { return fterm(v, c, mc); });
+  if (__ballot(own && !fast)) {
+    if (own && !fast) {
+      acc = 0.f;
+      accx = 0.f;
+      sum_terms([&](float v) { return term(v, m, c); });
+    }
   }
   __syncthreads();
   float M = ps.m[par][0];
