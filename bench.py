@@ -39,7 +39,10 @@ MAX_POOL = 16          # host cores a one-GPU machine gives this job
 # what the counter reads for a copy kernel of known size in the same run.
 # Keyed by the SHA-256 of the kernel source the counters were taken on: for
 # any other source the figure is stale and the bench reports null.
-TRAFFIC_BYTES: dict = {}
+TRAFFIC_BYTES: dict = {
+    # FETCH 71,906.9 KiB x 1.99963 + WRITE 346.7 KiB x 1.0 per launch
+    "c84f8f2652df0480dc2d709b7d519b5a3c2ad604df88001a2a0a19651ae41a17": 147593392,
+}
 
 # Workloads besides the headline one: (config, steps per repetition, label).
 OTHERS = [
@@ -65,6 +68,9 @@ def parse():
     ap.add_argument("--no-stream", action="store_true", help="skip the streaming-read ceiling")
     ap.add_argument("--graph", action="store_true",
                     help="replay the headline steps from a captured HIP graph")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device-to-device copy of 128 MiB, 10 times (the "
+                         "reference kernel that scales the HBM byte counters of a profiler run)")
     ap.add_argument("--only", type=int, choices=[c for c, _, _ in OTHERS],
                     help="time only this other workload (for profiler runs); prints its record")
     return ap.parse_args()
@@ -302,6 +308,21 @@ def parity(w, res):
     return out
 
 
+COPY_BYTES = 128 << 20
+
+
+def copy_calibration():
+    """A plain device-to-device copy of COPY_BYTES, ten times: the profiler's
+    FETCH_SIZE / WRITE_SIZE of this kernel against its known bytes give the
+    counters' scale on this GPU."""
+    import torch
+    src = torch.randint(0, 255, (COPY_BYTES,), dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
 def kernel_traffic():
     import hashlib
     with open(KERNEL_SRC, "rb") as f:
@@ -370,6 +391,8 @@ def main() -> int:
     torch.cuda.set_device(dev)
     binding.lib()                       # fails loudly without the HIP library
 
+    if args.copy_calibration:
+        copy_calibration()
     ms, times, res = time_workload(w, args.steps, args.warmup, args.reps, graph=args.graph)
     t = ms * 1e-3
     rows = w.total_rows
@@ -402,6 +425,9 @@ def main() -> int:
         "algorithmic_bytes_per_step": alg_bytes,
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": gbps / PEAK_HBM_GBPS, "traffic": kernel_traffic(),
+                     "traffic_unit": "HBM bytes per launch (profiler counters, scaled)",
+                     "traffic_GBps": (None if kernel_traffic() is None
+                                      else kernel_traffic() / t / 1e9),
                      "ceiling_GBps": None if ceiling is None else ceiling["GBps"],
                      "frac_of_ceiling": None if ceiling is None else gbps / ceiling["GBps"],
                      "timed": "one verify launch per step (the only kernel of the call on "

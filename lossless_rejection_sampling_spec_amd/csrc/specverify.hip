@@ -734,47 +734,53 @@ __device__ __forceinline__ CStat chunk_stats(Seg<T>& sg, bool greedy, float tau,
   // scale below takes out again; it stays harmless while |mc| < 2^30 (|err| <
   // 64).  Beyond that (a huge |m|, or a tiny temperature) the thread takes the
   // terms exp2((l - m) * c) instead, which cannot overflow for l <= m, and
-  // scales them to the chunk max by exp2((m - M) * c).
+  // scales them to the chunk max by exp2((m - M) * c).  The one-FMA loops
+  // always run (a per-thread choice between two loops slowed the common
+  // case); a wave that holds such a thread redoes it afterwards, on a
+  // wave-uniform branch.
   float acc = 0.f, accx = 0.f;
   const bool own = m > NEG_INF && m < POS_INF;
   const float mc = m * c;
   const bool fast = __builtin_fabsf(mc) < 1073741824.0f;
-  auto sum_terms = [&](auto tf) {
-    if (xl < 0) {
+  constexpr int VEC = VT<T>::VEC;
+  const int owner = xl >= 0 ? (xl / VEC) % WG : -1;
+  const int xslot = xl >= 0 ? ((xl / VEC) / WG) * VEC + xl % VEC : -1;
+  const int ix = ((int)threadIdx.x == owner) ? xslot : -1;
+  if (xl < 0) {
+    if (own) {
 #pragma unroll
-      for (int i = 0; i < EPT; ++i) acc += tf(sg.at(i));
+      for (int i = 0; i < EPT; ++i) acc += fterm(sg.at(i), c, mc);
+    }
+  } else if (own) {
+    if (before) {
+      // the terms of the elements that precede x in token order
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) {
+        const float e = fterm(sg.at(i), c, mc);
+        acc += e;
+        accx += (strided_index<T>(i) < xl) ? e : 0.f;
+      }
     } else {
-      constexpr int VEC = VT<T>::VEC;
-      const int owner = (xl / VEC) % WG;
-      const int xslot = ((xl / VEC) / WG) * VEC + xl % VEC;
-      const int ix = ((int)threadIdx.x == owner) ? xslot : -1;
-      if (before) {
-        // the terms of the elements that precede x in token order
 #pragma unroll
-        for (int i = 0; i < EPT; ++i) {
-          const float e = tf(sg.at(i));
-          acc += e;
-          accx += (strided_index<T>(i) < xl) ? e : 0.f;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < EPT; ++i) {
-          const float e = tf(sg.at(i));
-          acc += e;
-          accx += (i == ix) ? 0.f : e;
-        }
+      for (int i = 0; i < EPT; ++i) {
+        const float e = fterm(sg.at(i), c, mc);
+        acc += e;
+        accx += (i == ix) ? 0.f : e;
       }
     }
-  };
-  // the one-FMA loop always runs (a per-thread choice between the two loops
-  // slowed the common case); a wave with a thread beyond 2^30 redoes that
-  // thread's terms afterwards, on a wave-uniform branch
-  if (own) sum_terms([&](float v) { return fterm(v, c, mc); });
+  }
   if (__ballot(own && !fast)) {
     if (own && !fast) {
       acc = 0.f;
       accx = 0.f;
-      sum_terms([&](float v) { return term(v, m, c); });
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) {
+        const float e = term(sg.at(i), m, c);
+        acc += e;
+        accx += (xl < 0) ? 0.f
+                : before ? ((strided_index<T>(i) < xl) ? e : 0.f)
+                         : ((i == ix) ? 0.f : e);
+      }
     }
   }
   __syncthreads();
