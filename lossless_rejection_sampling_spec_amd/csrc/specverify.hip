@@ -90,6 +90,9 @@ constexpr float NEG_INF = -__builtin_inff();
 constexpr float POS_INF = __builtin_inff();
 constexpr double LOG2E = 1.4426950408889634;
 constexpr uint32_t TAG = 0x80000000u;     // "fresh" bit of a hand-off word (high half)
+// high half of a threshold word: the threshold kernel published the row's
+// statistics itself (the row's producers have nothing to do)
+constexpr uint32_t THR_PUBLISHED = 1u;
 constexpr uint32_t F_NONE = 0x40000000u;  // helper decision: no residual to compute
 constexpr uint32_t F_BAD = 0x20000000u;   // residual chunk saw an invalid probability
 // Words of one helper's decision record: 0 the target chunk max (the stop
@@ -884,10 +887,8 @@ __device__ __forceinline__ void produce(const Params& P, const Req& R, int b, in
   // request's parameters, which only decide whether they are used
   const int xr = j < k ? ldu(P.drafts + d0 + j) : -1;
   const float tau_r = P.thr_t ? thr_of(P.thr_t, row) : NEG_INF;
-  const float taud_r = (P.thr_d && j < k) ? thr_of(P.thr_d, d0 + j) : NEG_INF;
   const float tau = R.filt ? tau_r : NEG_INF;
   const TD* drow = (const TD*)P.draft + (int64_t)(d0 + j) * P.ld_d;
-  const float taud = (R.kind == SV_DRAFT_LOGITS && j < k && R.filt) ? taud_r : NEG_INF;
   const int x = R.greedy ? -1 : xr;
   const int c_begin = s * P.S;
   const int c_end = min(c_begin + P.S, nc);
@@ -928,15 +929,13 @@ __device__ __forceinline__ void produce(const Params& P, const Req& R, int b, in
       put_w(P.rx + (int64_t)row * 3 + 1, 0u, ps.pub[tp][2]);
   }
   if (xs) {
-    float lx = to_f(lx_raw), ldx = to_f(ldx_raw);
+    // the draft value at x goes out raw: a draft logit is masked by the
+    // finalizer, which reads the draft row's threshold
+    float lx = to_f(lx_raw);
     if (lx < tau) lx = NEG_INF;
     put_w(P.rx + (int64_t)row * 3 + 0, 0u, __float_as_uint(lx));
-    if (R.kind == SV_DRAFT_PROBS) {
-      put_w(P.rx + (int64_t)row * 3 + 2, 0u, __float_as_uint(ldx));
-    } else if (R.kind == SV_DRAFT_LOGITS) {
-      if (ldx < taud) ldx = NEG_INF;
-      put_w(P.rx + (int64_t)row * 3 + 2, 0u, __float_as_uint(ldx));
-    }
+    if (R.kind == SV_DRAFT_PROBS || R.kind == SV_DRAFT_LOGITS)
+      put_w(P.rx + (int64_t)row * 3 + 2, 0u, __float_as_uint(to_f(ldx_raw)));
   }
 }
 
@@ -1362,7 +1361,9 @@ __device__ __forceinline__ void finalize(const Params& P, int b, int cu0, int k,
         const double ex = exp2(((double)fs.lx[j] - (double)M) * R.ce);   // e_x in row-max units
         px = ex / S;
         if (logits) {
-          qx = exp2(((double)fs.dlx[j] - (double)Mq) * R.ce) / Sq;
+          float dl = fs.dlx[j];
+          if (R.filt && P.thr_d && dl < thr_of(P.thr_d, d0 + j)) dl = NEG_INF;
+          qx = exp2(((double)dl - (double)Mq) * R.ce) / Sq;
         } else if (R.kind == SV_DRAFT_PROBS) {
           qx = (double)fs.dlx[j];
           if (!(qx >= 0.0 && qx < (double)POS_INF)) nonfin = true;
@@ -1982,6 +1983,9 @@ __global__ __launch_bounds__(WG, 4) void k_verify(const Params P) {
       const int cu0 = ldu(P.cu + b), cu1 = ldu(P.cu + b + 1);
       if (R.greedy || R.bad_param || R.kind != SV_DRAFT_LOGITS || j >= cu1 - cu0 - 1) return;
       if (!offsets_ok<E>(P, b, cu0, cu1)) return;
+      // the threshold kernel wrote this row's word in this call (same
+      // conditions), and published its statistics when it says so
+      if (R.filt && P.thr_d && hi32(ldu(P.thr_d + (cu0 - b + j))) == THR_PUBLISHED) return;
       Buf<TT, TD> A;
       issue_task<TT, TD, AL>((const TT*)nullptr, (const TD*)P.draft + (int64_t)(cu0 - b + j) * P.ld_d,
                              true, s * P.S, P.vocab, A);
@@ -2015,12 +2019,21 @@ __global__ __launch_bounds__(WG, 4) void k_verify(const Params P) {
     return;
   }
   if (j > k) return;
+  // a filtered row whose statistics the threshold kernel published (it wrote
+  // the row's word in this call under the same conditions) needs no strip;
   // the strip's first chunk is requested before the request's parameters
+  const bool pub = P.thr_t && hi32(ldu(P.thr_t + cu0 + j)) == THR_PUBLISHED;
   Buf<TT, TD> A;
-  issue_task<TT, TD, AL>(target_rows<TT>(P, pen_of(P, b)) + (int64_t)(cu0 + j) * P.ld_t,
-                         (const TD*)nullptr, false, s * P.S, P.vocab, A);
+  if (!pub)
+    issue_task<TT, TD, AL>(target_rows<TT>(P, pen_of(P, b)) + (int64_t)(cu0 + j) * P.ld_t,
+                           (const TD*)nullptr, false, s * P.S, P.vocab, A);
   const Req R = load_req(P, b);
-  if (!R.bad_param) produce<TT, TD, AL>(P, R, b, cu0, k, j, s, ps, A);
+  if (!R.bad_param && !(pub && R.filt && !R.greedy)) {
+    if (pub)   // a word left from an earlier call: the strip runs after all
+      issue_task<TT, TD, AL>(target_rows<TT>(P, R.pen) + (int64_t)(cu0 + j) * P.ld_t,
+                             (const TD*)nullptr, false, s * P.S, P.vocab, A);
+    produce<TT, TD, AL>(P, R, b, cu0, k, j, s, ps, A);
+  }
   if (j == k && s == P.ns - 1) finalize<TT, TD, AL>(P, b, cu0, k, R, sm, fs, ds, stage);
 }
 
@@ -2067,8 +2080,32 @@ constexpr int TNW = TW / 64;
 constexpr int THR_NL = 16;        // 128-bit words per thread of a row kept in registers
 constexpr int HCOPY = 32;         // histogram copies
 constexpr int LIST_BYTES = 65536; // LDS for the candidate keys of a row
-// candidate keys a row may keep: bf16 keys are stored in 16 bits
-template <typename T> constexpr unsigned list_cap() { return LIST_BYTES / (sizeof(T) == 2 ? 2 : 4); }
+// List entries.  bf16: 32 bits, the key's upper half over the value's place
+// within its wave's share of the row (word i, lane, value h: 13 bits; the
+// wave is the list segment's); fp32: 64 bits, the key below the element index.
+template <typename T> struct LE;
+template <> struct LE<uint16_t> {
+  using E = uint32_t;
+  static constexpr unsigned CAP = LIST_BYTES / 4;
+  // element e = (i * TW + wave * 64 + lane) * 8 + h lives at (i, lane, h)
+  __device__ static E make(uint32_t key, int e) {
+    return key | ((((uint32_t)e >> 4) & ~511u) | ((uint32_t)e & 511u));
+  }
+  __device__ static uint32_t key(E en) { return en & 0xffff0000u; }
+  __device__ static int index(E en, int wave) {
+    const uint32_t l = en & 0xffffu;
+    return (int)((l >> 9) * (TW * 8) + (uint32_t)wave * 512u + (l & 511u));
+  }
+};
+template <> struct LE<float> {
+  using E = unsigned long long;
+  static constexpr unsigned CAP = LIST_BYTES / 8;
+  __device__ static E make(uint32_t key, int e) { return ((E)(uint32_t)e << 32) | key; }
+  __device__ static uint32_t key(E en) { return (uint32_t)en; }
+  __device__ static int index(E en, int) { return (int)(en >> 32); }
+};
+template <typename T> constexpr unsigned list_cap() { return LE<T>::CAP; }
+constexpr int REG_NC = THR_NL * TW * 8 / CHUNK;   // chunks of a row kept in registers (bf16: 16)
 constexpr int EBINS = 64;         // exponent bins of the top-p bound
 
 // Keys: the value's bits with the sign bit flipped for non-negative values
@@ -2096,8 +2133,11 @@ struct ThrShared {
   } h;
   union {
     uint32_t k32[LIST_BYTES / 4];
-    uint16_t k16[LIST_BYTES / 2];
-  } list;                                // candidate keys
+    unsigned long long k64[LIST_BYTES / 8];
+  } list;                                // candidates (LE<T> entries)
+  uint32_t cmax[REG_NC];                 // published statistics: chunk max keys,
+  unsigned long long csum[REG_NC];       // chunk masses (units of 2^-40) and
+  unsigned long long csx;                // the mass of the draft id's chunk without it
   double eb[EBINS];                      // merged exponent bins
   unsigned wcnt[TNW];                    // list entries appended by each wave
   alignas(16) unsigned long long bins[256];   // merged bins of the level
@@ -2110,6 +2150,12 @@ struct ThrShared {
   int digit;
 };
 
+template <typename T>
+__device__ __forceinline__ typename LE<T>::E* list_of(ThrShared& th) {
+  if constexpr (sizeof(T) == 2) return th.list.k32;
+  else return th.list.k64;
+}
+
 // round(t * 2^40) for t in [0, 1]: t * 2^40 is exact in fp32, rintf rounds it
 // to nearest even (values of 2^23 and above are integers already), and the two
 // 32-bit halves of the integer are exact in fp32 too
@@ -2120,17 +2166,33 @@ __device__ __forceinline__ unsigned long long fixmass(float t) {
   return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
-// f(v) for the values of one 128-bit word of a row, in element order.
+// f(v, e) for the values of one 128-bit word of a row, in element order; e
+// is the element index (e0: the word's first).
 template <typename T, typename F>
-__device__ __forceinline__ void each_val(const uint4& w, F& f) {
+__device__ __forceinline__ void each_val(const uint4& w, int e0, F& f) {
   const uint32_t d[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
     if constexpr (sizeof(T) == 4) {
-      f(__uint_as_float(d[h]));
+      f(__uint_as_float(d[h]), e0 + h);
     } else {
-      f(__uint_as_float(d[h] << 16));
-      f(__uint_as_float(d[h] & 0xffff0000u));
+      f(__uint_as_float(d[h] << 16), e0 + 2 * h);
+      f(__uint_as_float(d[h] & 0xffff0000u), e0 + 2 * h + 1);
+    }
+  }
+}
+
+// The VEC values of a word in element order.
+template <typename T>
+__device__ __forceinline__ void unpack_word(const uint4& w, float* v) {
+  const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    if constexpr (sizeof(T) == 4) {
+      v[h] = __uint_as_float(d[h]);
+    } else {
+      v[2 * h] = __uint_as_float(d[h] << 16);
+      v[2 * h + 1] = __uint_as_float(d[h] & 0xffff0000u);
     }
   }
 }
@@ -2295,31 +2357,46 @@ __device__ __forceinline__ void pick_digit(ThrShared& th, int lev, unsigned K, f
 // Radix select over the keys of the list: the K-th largest key (MASS false),
 // or the key of the top-p cut of the keys at or above kfloor (MASS true; z the
 // total mass of the set the cut is taken in, or < 0 for the listed keys').
+// A list of at most LIST_SMALL entries adds straight into the merged bins
+// (one copy: few atomics meet on one address), a longer one into the copies.
+constexpr unsigned LIST_SMALL = 2048;
 template <typename T, bool MASS>
-__device__ __forceinline__ uint32_t list_select(ThrShared& th, unsigned K, float Pp, double z,
-                                                uint32_t kfloor, float M, float c) {
+__device__ __forceinline__ uint32_t list_select(ThrShared& th, unsigned n, unsigned K, float Pp,
+                                                double z, uint32_t kfloor, float M, float c) {
   constexpr int LEVELS = sizeof(T) == 2 ? 2 : 4;
   const int cp = threadIdx.x & (HCOPY - 1);
+  const bool small = n <= LIST_SMALL;
+  const typename LE<T>::E* lst = list_of<T>(th);
   uint32_t prefix = 0u, pmask = 0u;
 #pragma unroll
   for (int lev = 0; lev < LEVELS; ++lev) {
     const int shift = 24 - 8 * lev;
-    clear_bins(th);
+    if (small) {
+      if (threadIdx.x < 256) th.bins[threadIdx.x] = 0ull;
+      __syncthreads();
+    } else {
+      clear_bins(th);
+    }
     // each wave walks its own segment of the list
     const int wv = threadIdx.x >> 6;
     const unsigned seg = list_cap<T>() / TNW;
     const unsigned nw = th.wcnt[wv];
     for (unsigned i = (threadIdx.x & 63); i < nw; i += 64) {
-      const unsigned at = wv * seg + i;
-      const uint32_t k = sizeof(T) == 2 ? (uint32_t)th.list.k16[at] << 16 : th.list.k32[at];
+      const uint32_t k = LE<T>::key(lst[wv * seg + i]);
       if (k >= kfloor && (k & pmask) == prefix) {
-        const uint32_t bin = ((k >> shift) & 255u) * HCOPY + cp;
-        if constexpr (MASS) atomicAdd(&th.h.m[bin], fixmass(term(keyv<T>(k), M, c)));
-        else atomicAdd(&th.h.c[bin], 1u);
+        const uint32_t d = (k >> shift) & 255u;
+        if constexpr (MASS) {
+          const unsigned long long f = fixmass(term(keyv<T>(k), M, c));
+          if (small) atomicAdd(&th.bins[d], f);
+          else atomicAdd(&th.h.m[d * HCOPY + cp], f);
+        } else {
+          if (small) atomicAdd(&th.bins[d], 1ull);
+          else atomicAdd(&th.h.c[d * HCOPY + cp], 1u);
+        }
       }
     }
     __syncthreads();
-    merge_bins<MASS>(th);
+    if (!small) merge_bins<MASS>(th);
     pick_digit<MASS>(th, lev, K, Pp, z);
     prefix |= (uint32_t)th.digit << shift;
     pmask |= 255u << shift;
@@ -2327,12 +2404,68 @@ __device__ __forceinline__ uint32_t list_select(ThrShared& th, unsigned K, float
   return prefix;
 }
 
+// Statistics of a row whose kept values are all on the list (keys >= tkey):
+// per chunk the max and the sum of exp2((v - m_c) c) under the threshold, as
+// the producers of k_verify publish them (one self-tagged word per chunk at
+// stat), and for the chunk that holds the draft id x the same sum without x
+// (prefix-match requests: of the values before x) at sxw.  Maxima by an
+// integer max over the keys; masses as integers in units of 2^-40, so the
+// sums do not depend on the order of the atomics.
+template <typename T>
+__device__ __forceinline__ void publish_stats(ThrShared& th, uint32_t tkey, float c, int nc, int x,
+                                              bool match, u64* stat, u64* sxw) {
+  const int tid = threadIdx.x;
+  const int wv = tid >> 6;
+  const unsigned seg = list_cap<T>() / TNW;
+  const unsigned nw = th.wcnt[wv];
+  if (tid < REG_NC) {
+    th.cmax[tid] = 0u;
+    th.csum[tid] = 0ull;
+  }
+  if (tid == 0) th.csx = 0ull;
+  __syncthreads();
+  const typename LE<T>::E* lst = list_of<T>(th);
+  for (unsigned i = (tid & 63); i < nw; i += 64) {
+    const typename LE<T>::E en = lst[wv * seg + i];
+    const uint32_t k = LE<T>::key(en);
+    if (k >= tkey) atomicMax(&th.cmax[LE<T>::index(en, wv) / CHUNK], k);
+  }
+  __syncthreads();
+  const int xc = x >= 0 ? x / CHUNK : -1;
+  for (unsigned i = (tid & 63); i < nw; i += 64) {
+    const typename LE<T>::E en = lst[wv * seg + i];
+    const uint32_t k = LE<T>::key(en);
+    if (k >= tkey) {
+      const int e = LE<T>::index(en, wv);
+      const int cc = e / CHUNK;
+      const unsigned long long fx = fixmass(term(keyv<T>(k), keyv<T>(th.cmax[cc]), c));
+      atomicAdd(&th.csum[cc], fx);
+      if (cc == xc && (match ? e < x : e != x)) atomicAdd(&th.csx, fx);
+    }
+  }
+  __syncthreads();
+  constexpr double UNIT = 9.094947017729282e-13;   // 2^-40
+  if (tid < nc) {
+    const uint32_t mk = th.cmax[tid];   // no finite value has key 0
+    const float m = mk ? keyv<T>(mk) : NEG_INF;
+    const float sm = mk ? (float)((double)th.csum[tid] * UNIT) : 0.f;
+    put_w(stat + tid, __float_as_uint(sm) & ~TAG, __float_as_uint(m));
+  }
+  if (tid == 0 && sxw != nullptr && x >= 0)
+    put_w(sxw, 0u, __float_as_uint((float)((double)th.csx * UNIT)));
+}
+
 // The row's threshold in tau.  The variant that keeps the row in registers
 // (REG) returns false, with nothing written, where a full-row fallback is
 // needed; the caller then runs the variant that reads the row for each pass.
+// With stat != nullptr the register variant also publishes the row's
+// statistics (publish_stats) whenever its threshold came from a list, and
+// sets published.
 template <typename T, bool REG>
 __device__ __forceinline__ bool row_threshold(const T* __restrict__ rp, int V, bool al,
-                                              const Req& R, ThrShared& th, float& tau) {
+                                              const Req& R, ThrShared& th, float& tau,
+                                              u64* stat = nullptr, int x = -1,
+                                              u64* sxw = nullptr, bool* published = nullptr) {
   constexpr int VEC = VT<T>::VEC;
   constexpr int LEVELS = sizeof(T) == 2 ? 2 : 4;
   constexpr uint32_t KNEG = key_neg<T>();
@@ -2355,23 +2488,23 @@ __device__ __forceinline__ bool row_threshold(const T* __restrict__ rp, int V, b
       else w[i] = make_uint4(nw, nw, nw, nw);
     }
   }
-  // each_read(f): f(v) for every value of the thread (-inf past the row's
-  // end), read from the row eight words at a time
-  auto each_read = [&](auto&& f) {
+  // each_read_w(f): f(word, e0) for every word of the thread (e0 the index of
+  // the word's first value), read from the row eight words at a time.  The
+  // trip count is the same in every lane (f may use wave-wide operations):
+  // words past the row's end, and values past element V, read as -inf
+  auto each_read_w = [&](auto&& f) {
     const int ng = (V + VEC - 1) / VEC;
-    for (int g0 = tid; g0 < ng; g0 += 8 * TW) {
+    for (int base = 0; base < ng; base += 8 * TW) {
+      const int g0 = base + tid;
       uint4 q[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) q[i] = thr_word<T>(rp, min(g0 + i * TW, ng - 1), V, al);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint4 x = thr_mask<T>(q[i], g0 + i * TW, V);
-        if (g0 + i * TW < ng) each_val<T>(x, f);
-      }
+      for (int i = 0; i < 8; ++i) f(thr_mask<T>(q[i], g0 + i * TW, V), (g0 + i * TW) * VEC);
     }
   };
-  // each(f): the same from the registers when the row is kept there
-  auto each = [&](auto&& f) {
+  // each_w(f): the same from the registers when the row is kept there
+  auto each_w = [&](auto&& f) {
     if constexpr (REG) {
       // the words pass through an empty asm statement first: what a pass
       // derives from them does not depend on the level, and the compiler
@@ -2380,30 +2513,42 @@ __device__ __forceinline__ bool row_threshold(const T* __restrict__ rp, int V, b
       for (int i = 0; i < THR_NL; ++i)
         asm volatile("" : "+v"(w[i].x), "+v"(w[i].y), "+v"(w[i].z), "+v"(w[i].w));
 #pragma unroll
-      for (int i = 0; i < THR_NL; ++i) each_val<T>(w[i], f);
+      for (int i = 0; i < THR_NL; ++i) f(w[i], (i * TW + tid) * VEC);
     } else {
-      each_read(f);
+      each_read_w(f);
     }
   };
+  // each(f) / each_read(f): f(v, e) for every value
+  auto each = [&](auto&& f) { each_w([&](const uint4& x, int e0) { each_val<T>(x, e0, f); }); };
+  auto each_read = [&](auto&& f) {
+    each_read_w([&](const uint4& x, int e0) { each_val<T>(x, e0, f); });
+  };
   // fill_list(vlo): every value at or above vlo goes to the list, each wave's
-  // to its own segment in order; the wave's count stays in a register.
-  // Returns the number of entries, or a number above the capacity when a
-  // segment overflowed.
+  // to its own segment, word by word (a word's values at consecutive places
+  // from the lane's offset in the wave's prefix sum of the counts); the
+  // wave's count stays in a register.  Returns the number of entries, or a
+  // number above the capacity when a segment overflowed.
   constexpr unsigned SEG = list_cap<T>() / TNW;
   auto fill_list = [&](float vlo) -> unsigned {
-    const unsigned sbase = (unsigned)(tid >> 6) * SEG;
+    typename LE<T>::E* lst = list_of<T>(th) + (unsigned)(tid >> 6) * SEG;
     unsigned wc = 0u;
-    each([&](float v) {
-      const bool hit = v >= vlo;
-      const uint64_t m = __ballot(hit);
-      if (m) {
-        const unsigned pos =
-            wc + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-        if (hit && pos < SEG) {
-          if constexpr (sizeof(T) == 2) th.list.k16[sbase + pos] = (uint16_t)(vkey<T>(v) >> 16);
-          else th.list.k32[sbase + pos] = vkey<T>(v);
+    each_w([&](const uint4& x, int e0) {
+      float v[VEC];
+      int cnt = 0;
+      unpack_word<T>(x, v);
+#pragma unroll
+      for (int h = 0; h < VEC; ++h) cnt += v[h] >= vlo ? 1 : 0;
+      if (__ballot(cnt != 0)) {
+        const int inc = wave_scan_add(cnt);
+        unsigned pos = wc + (unsigned)(inc - cnt);
+#pragma unroll
+        for (int h = 0; h < VEC; ++h) {
+          if (v[h] >= vlo) {
+            if (pos < SEG) lst[pos] = LE<T>::make(vkey<T>(v[h]), e0 + h);
+            ++pos;
+          }
         }
-        wc += (unsigned)__popcll(m);
+        wc += (unsigned)__builtin_amdgcn_readlane(inc, 63);
       }
     });
     if (lane == 0) th.wcnt[tid >> 6] = wc;
@@ -2417,14 +2562,9 @@ __device__ __forceinline__ bool row_threshold(const T* __restrict__ rp, int V, b
     return big > SEG ? list_cap<T>() + 1u : n;
   };
 
-  // row max and each thread's own max.  A row that holds a NaN or +inf is
-  // reported as a fault by the row pass whatever its threshold, so the max
-  // need not propagate NaN (a plain max is one instruction); +inf or a row of
-  // -inf leaves the row unfiltered.  bf16: the upper value of a word is
-  // compared with the lower one's bits still below it (they perturb it by
-  // less than one bf16 step, so the largest word holds the largest value,
-  // masked once at the end; a word whose upper value is +-inf reads as NaN
-  // and is skipped, harmlessly)
+  // row max and each thread's own max, NaN-propagating: a row that holds a
+  // NaN or +inf, or only -inf, is left unfiltered and unpublished, and the
+  // row pass of the verify kernel reports it
   float tmax = NEG_INF;
   {
     float mh = NEG_INF, ml = NEG_INF;
@@ -2433,10 +2573,10 @@ __device__ __forceinline__ bool row_threshold(const T* __restrict__ rp, int V, b
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         if constexpr (sizeof(T) == 2) {
-          mh = __builtin_fmaxf(mh, __uint_as_float(d[h]));
-          ml = __builtin_fmaxf(ml, __uint_as_float(d[h] << 16));
+          mh = fmax3nan(mh, __uint_as_float(d[h] & 0xffff0000u));
+          ml = fmax3nan(ml, __uint_as_float(d[h] << 16));
         } else {
-          mh = __builtin_fmaxf(mh, __uint_as_float(d[h]));
+          mh = fmax3nan(mh, __uint_as_float(d[h]));
         }
       }
     };
@@ -2447,8 +2587,7 @@ __device__ __forceinline__ bool row_threshold(const T* __restrict__ rp, int V, b
       const int ng = (V + VEC - 1) / VEC;
       for (int g = tid; g < ng; g += TW) wmax(thr_mask<T>(thr_word<T>(rp, g, V, al), g, V));
     }
-    if constexpr (sizeof(T) == 2) mh = __uint_as_float(__float_as_uint(mh) & 0xffff0000u);
-    tmax = __builtin_fmaxf(mh, ml);
+    tmax = fmax3nan(mh, ml);
   }
   const float M = thr_block_max(tmax, th);
   tau = NEG_INF;
@@ -2462,21 +2601,24 @@ __device__ __forceinline__ bool row_threshold(const T* __restrict__ rp, int V, b
     const unsigned K = (unsigned)R.K;
     bool full = true;      // full-row passes
     if (K <= (unsigned)TW) {
-      // the K-th largest of the threads' maxima: K values are at or above it
+      // a lower bound of the K-th largest value: each wave finds the r-th
+      // largest of its threads' maxima, r = ceil(K / 16), by a binary search
+      // over the key bits with ballot counts; r values of the wave are at or
+      // above it, so K values are at or above the smallest of the 16
+      const unsigned r = (K + TNW - 1) / TNW;
       const uint32_t kt = vkey<T>(tmax);
-      uint32_t prefix = 0u, pmask = 0u;
+      uint32_t t = 0u;
 #pragma unroll
-      for (int lev = 0; lev < LEVELS; ++lev) {
-        const int shift = 24 - 8 * lev;
-        clear_bins(th);
-        if ((kt & pmask) == prefix) atomicAdd(&th.h.c[((kt >> shift) & 255u) * HCOPY + cp], 1u);
-        __syncthreads();
-        merge_bins<false>(th);
-        pick_digit<false>(th, lev, K, 0.f);
-        prefix |= (uint32_t)th.digit << shift;
-        pmask |= 255u << shift;
+      for (int bit = 31; bit >= (sizeof(T) == 2 ? 16 : 0); --bit) {
+        const uint32_t cand = t | (1u << bit);
+        if ((unsigned)__popcll(__ballot(kt >= cand)) >= r) t = cand;
       }
-      const float lb = keyv<T>(prefix);
+      if (lane == 0) th.cw[tid >> 6] = t;
+      __syncthreads();
+      uint32_t lbk = 0xffffffffu;
+#pragma unroll
+      for (int q = 0; q < TNW; ++q) lbk = min(lbk, (uint32_t)th.cw[q]);
+      const float lb = keyv<T>(lbk);
       if (lb > NEG_INF) {
         const unsigned n = fill_list(lb);
         if (n <= list_cap<T>()) {
@@ -2486,13 +2628,13 @@ __device__ __forceinline__ bool row_threshold(const T* __restrict__ rp, int V, b
             // exactly K candidates: K is below the number of finite values
             // only if a finite value lies below the bound
             unsigned long long below = 0ull;
-            each([&](float v) { below += (v > NEG_INF && v < lb) ? 1ull : 0ull; });
+            each([&](float v, int) { below += (v > NEG_INF && v < lb) ? 1ull : 0ull; });
             keep_all = thr_block_sum(below, th) == 0ull;
           }
           if (keep_all) {
             do_k = false;
           } else {
-            tau_key = list_select<T, false>(th, K, 0.f, -1.0, 0u, M, R.c);
+            tau_key = list_select<T, false>(th, n, K, 0.f, -1.0, 0u, M, R.c);
             n_list = n;
           }
         }
@@ -2508,7 +2650,7 @@ __device__ __forceinline__ bool row_threshold(const T* __restrict__ rp, int V, b
         const int shift = 24 - 8 * lev;
         clear_bins(th);
         // -inf and the padding land in digit 0 at level 0
-        each_read([&](float v) {
+        each_read([&](float v, int) {
           const uint32_t k = vkey<T>(v);
           if ((k & pmask) == prefix) atomicAdd(&th.h.c[((k >> shift) & 255u) * HCOPY + cp], 1u);
         });
@@ -2527,7 +2669,7 @@ __device__ __forceinline__ bool row_threshold(const T* __restrict__ rp, int V, b
           __syncthreads();
           if (th.upper <= (unsigned long long)K) {
             unsigned long long n = 0ull;
-            each_read([&](float v) { n += (v == NEG_INF) ? 1ull : 0ull; });
+            each_read([&](float v, int) { n += (v == NEG_INF) ? 1ull : 0ull; });
             ninf = thr_block_sum(n, th);
             if ((unsigned long long)K >= th.upper + th.bins[0] - ninf) {
               do_k = false;
@@ -2550,7 +2692,7 @@ __device__ __forceinline__ bool row_threshold(const T* __restrict__ rp, int V, b
     bool full = true;
     if (do_k && n_list != 0u) {
       // the top-k set is on the list
-      pk = list_select<T, true>(th, 0u, R.P, -1.0, tau_key, M, R.c);
+      pk = list_select<T, true>(th, n_list, 0u, R.P, -1.0, tau_key, M, R.c);
       full = false;
     } else if (!do_k) {
       // the total mass, exact, and the terms by binary exponent: bin b holds
@@ -2559,7 +2701,7 @@ __device__ __forceinline__ bool row_threshold(const T* __restrict__ rp, int V, b
       double zs = 0.0;
       float zw = 0.f;
       int nz = 0;
-      each([&](float v) {
+      each([&](float v, int) {
         const float t = term(v, M, R.c);
         zw += t;
         if (++nz == VEC) {   // a word's values (a compile-time count when unrolled)
@@ -2601,7 +2743,7 @@ __device__ __forceinline__ bool row_threshold(const T* __restrict__ rp, int V, b
       if (bc < EBINS - 1 && vlo > NEG_INF) {
         const unsigned n = fill_list(vlo);
         if (n <= list_cap<T>()) {
-          pk = list_select<T, true>(th, 0u, R.P, (double)Z, 0u, M, R.c);
+          pk = list_select<T, true>(th, n, 0u, R.P, (double)Z, 0u, M, R.c);
           full = false;
         }
       }
@@ -2616,7 +2758,7 @@ __device__ __forceinline__ bool row_threshold(const T* __restrict__ rp, int V, b
       for (int lev = 0; lev < LEVELS; ++lev) {
         const int shift = 24 - 8 * lev;
         clear_bins(th);
-        each_read([&](float v) {
+        each_read([&](float v, int) {
           const uint32_t k = vkey<T>(v);
           if (k >= kfloor && (k & pmask) == prefix)
             atomicAdd(&th.h.m[((k >> shift) & 255u) * HCOPY + cp], fixmass(term(v, M, R.c)));
@@ -2632,15 +2774,28 @@ __device__ __forceinline__ bool row_threshold(const T* __restrict__ rp, int V, b
     tau_key = pk > tau_key ? pk : tau_key;
   }
   tau = (do_k || do_p) ? keyv<T>(tau_key) : NEG_INF;
+  if constexpr (REG) {
+    // every selection of this variant ran on the list, so the kept values
+    // (keys >= tau_key) are all on it
+    if (stat != nullptr && (do_k || do_p)) {
+      publish_stats<T>(th, tau_key, R.c, (V + CHUNK - 1) / CHUNK, x, R.kind == SV_DRAFT_MATCH,
+                       stat, sxw);
+      *published = true;
+    }
+  }
   return true;
 }
 
 template <typename T>
 __device__ __forceinline__ float thr_row(const T* __restrict__ rp, int64_t ld, int V, const Req& R,
-                                         ThrShared& th) {
+                                         ThrShared& th, u64* stat, int x, u64* sxw,
+                                         bool& published) {
   const bool al = (((uintptr_t)rp & 15) == 0) && (((ld * (int64_t)sizeof(T)) & 15) == 0);
   float tau = NEG_INF;
-  if (al && V <= THR_NL * TW * VT<T>::VEC && row_threshold<T, true>(rp, V, true, R, th, tau)) return tau;
+  published = false;
+  if (al && V <= THR_NL * TW * VT<T>::VEC &&
+      row_threshold<T, true>(rp, V, true, R, th, tau, stat, x, sxw, &published))
+    return tau;
   __syncthreads();   // the register variant's last LDS reads are done
   row_threshold<T, false>(rp, V, al, R, th, tau);
   return tau;
@@ -2663,19 +2818,36 @@ __global__ __launch_bounds__(TW) void k_thresh(const Params P) {
   if (j > k || R.greedy || R.bad_param || !R.filt) return;
   if (side == 1 && (R.kind != SV_DRAFT_LOGITS || j >= k)) return;
   if (!offsets_ok<E>(P, b, cu0, cu1)) return;
-  u64* out = side == 0 ? P.thr_t + cu0 + j : P.thr_d + (cu0 - b + j);
+  const int d0 = cu0 - b;
+  u64* out = side == 0 ? P.thr_t + cu0 + j : P.thr_d + (d0 + j);
+  // the statistics words of the row, and for a target row with a draft id in
+  // range the words of the values at it
+  u64* stat = side == 0 ? P.cst + (int64_t)(cu0 + j) * P.nc : P.dst + (int64_t)(d0 + j) * P.nc;
+  const int xr = (side == 0 && j < k) ? ldu(P.drafts + d0 + j) : -1;
+  const int x = (xr >= 0 && xr < P.vocab) ? xr : -1;
+  u64* rx = P.rx + (int64_t)(cu0 + j) * 3;
+  const TT* trow = target_rows<TT>(P, R.pen) + (int64_t)(cu0 + j) * P.ld_t;
+  const TD* drow = (const TD*)P.draft + (int64_t)(d0 + j) * P.ld_d;
   float tau;
+  bool pub;
   if constexpr (std::is_same<TT, TD>::value) {   // one copy of the code for both sides
-    const TT* rp = side == 0 ? target_rows<TT>(P, R.pen) + (int64_t)(cu0 + j) * P.ld_t
-                             : (const TT*)P.draft + (int64_t)(cu0 - b + j) * P.ld_d;
-    tau = thr_row<TT>(rp, side == 0 ? P.ld_t : P.ld_d, P.vocab, R, th);
+    tau = thr_row<TT>(side == 0 ? trow : drow, side == 0 ? P.ld_t : P.ld_d, P.vocab, R, th, stat,
+                      x, x >= 0 ? rx + 1 : nullptr, pub);
   } else if (side == 0) {
-    tau = thr_row<TT>(target_rows<TT>(P, R.pen) + (int64_t)(cu0 + j) * P.ld_t, P.ld_t, P.vocab,
-                      R, th);
+    tau = thr_row<TT>(trow, P.ld_t, P.vocab, R, th, stat, x, x >= 0 ? rx + 1 : nullptr, pub);
   } else {
-    tau = thr_row<TD>((const TD*)P.draft + (int64_t)(cu0 - b + j) * P.ld_d, P.ld_d, P.vocab, R, th);
+    tau = thr_row<TD>(drow, P.ld_d, P.vocab, R, th, stat, -1, nullptr, pub);
   }
-  if (threadIdx.x == 0) *out = (u64)__float_as_uint(tau);
+  if (threadIdx.x == 0) {
+    if (pub && x >= 0) {
+      float lx = to_f(trow[x]);
+      if (lx < tau) lx = NEG_INF;
+      put_w(rx + 0, 0u, __float_as_uint(lx));
+      if (R.kind == SV_DRAFT_LOGITS || R.kind == SV_DRAFT_PROBS)
+        put_w(rx + 2, 0u, __float_as_uint(to_f(drow[x])));
+    }
+    *out = ((u64)(pub ? THR_PUBLISHED : 0u) << 32) | (u64)__float_as_uint(tau);
+  }
 }
 
 // ---------------------------------------------------------------------------
