@@ -2079,19 +2079,21 @@ constexpr int TW = 1024;          // threads of a threshold workgroup
 constexpr int TNW = TW / 64;
 constexpr int THR_NL = 16;        // 128-bit words per thread of a row kept in registers
 constexpr int HCOPY = 32;         // histogram copies
-constexpr int LIST_BYTES = 65536; // LDS for the candidate keys of a row
-// List entries.  bf16: 32 bits, the key's upper half over the value's place
-// within its wave's share of the row (word i, lane, value h: 13 bits; the
-// wave is the list segment's); fp32: 64 bits, the key below the element index.
+constexpr int LIST_BYTES = 90112; // LDS for the candidates of a row
+// List entries: the value's bits (-0 folded into +0) and its place.  bf16: 32
+// bits, the value's upper half over its place within its wave's share of the
+// row (word i, lane, value h: 13 bits; the wave is the list segment's); fp32:
+// 64 bits, the value's bits below the element index.
 template <typename T> struct LE;
 template <> struct LE<uint16_t> {
   using E = uint32_t;
   static constexpr unsigned CAP = LIST_BYTES / 4;
-  // element e = (i * TW + wave * 64 + lane) * 8 + h lives at (i, lane, h)
-  __device__ static E make(uint32_t key, int e) {
-    return key | ((((uint32_t)e >> 4) & ~511u) | ((uint32_t)e & 511u));
+  // element e = (i * TW + wave * 64 + lane) * 8 + h lives at (i, lane, h);
+  // bits: a bf16 value's fp32 bits (lower half zero)
+  __device__ static E make(uint32_t bits, int e) {
+    return bits | ((((uint32_t)e >> 4) & ~511u) | ((uint32_t)e & 511u));
   }
-  __device__ static uint32_t key(E en) { return en & 0xffff0000u; }
+  __device__ static uint32_t bits(E en) { return en & 0xffff0000u; }
   __device__ static int index(E en, int wave) {
     const uint32_t l = en & 0xffffu;
     return (int)((l >> 9) * (TW * 8) + (uint32_t)wave * 512u + (l & 511u));
@@ -2100,8 +2102,8 @@ template <> struct LE<uint16_t> {
 template <> struct LE<float> {
   using E = unsigned long long;
   static constexpr unsigned CAP = LIST_BYTES / 8;
-  __device__ static E make(uint32_t key, int e) { return ((E)(uint32_t)e << 32) | key; }
-  __device__ static uint32_t key(E en) { return (uint32_t)en; }
+  __device__ static E make(uint32_t bits, int e) { return ((E)(uint32_t)e << 32) | bits; }
+  __device__ static uint32_t bits(E en) { return (uint32_t)en; }
   __device__ static int index(E en, int) { return (int)(en >> 32); }
 };
 template <typename T> constexpr unsigned list_cap() { return LE<T>::CAP; }
@@ -2125,6 +2127,10 @@ __device__ __forceinline__ float keyv(uint32_t k) {
   return __uint_as_float(sizeof(T) == 2 ? (u & 0xffff0000u) : u);
 }
 template <typename T> constexpr uint32_t key_neg() { return sizeof(T) == 2 ? 0x007f0000u : 0x007fffffu; }
+template <typename T>
+__device__ __forceinline__ uint32_t lkey(typename LE<T>::E en) {
+  return vkey<T>(__uint_as_float(LE<T>::bits(en)));
+}
 
 struct ThrShared {
   union {
@@ -2135,6 +2141,7 @@ struct ThrShared {
     uint32_t k32[LIST_BYTES / 4];
     unsigned long long k64[LIST_BYTES / 8];
   } list;                                // candidates (LE<T> entries)
+  unsigned long long sink[64];           // where a lane's non-candidates are written
   uint32_t cmax[REG_NC];                 // published statistics: chunk max keys,
   unsigned long long csum[REG_NC];       // chunk masses (units of 2^-40) and
   unsigned long long csx;                // the mass of the draft id's chunk without it
@@ -2382,7 +2389,7 @@ __device__ __forceinline__ uint32_t list_select(ThrShared& th, unsigned n, unsig
     const unsigned seg = list_cap<T>() / TNW;
     const unsigned nw = th.wcnt[wv];
     for (unsigned i = (threadIdx.x & 63); i < nw; i += 64) {
-      const uint32_t k = LE<T>::key(lst[wv * seg + i]);
+      const uint32_t k = lkey<T>(lst[wv * seg + i]);
       if (k >= kfloor && (k & pmask) == prefix) {
         const uint32_t d = (k >> shift) & 255u;
         if constexpr (MASS) {
@@ -2410,12 +2417,24 @@ __device__ __forceinline__ uint32_t list_select(ThrShared& th, unsigned n, unsig
 // stat), and for the chunk that holds the draft id x the same sum without x
 // (prefix-match requests: of the values before x) at sxw.  Maxima by an
 // integer max over the keys; masses as integers in units of 2^-40, so the
-// sums do not depend on the order of the atomics.
+// sums do not depend on the order of the atomics.  A wave's segment is in
+// element order, so 64 consecutive entries mostly share a chunk: such a
+// window is reduced across the wave first and takes one atomic.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, (uint32_t)dpp_i<DPP_XOR1>((int)x));
+  x = max(x, (uint32_t)dpp_i<DPP_XOR2>((int)x));
+  x = max(x, (uint32_t)dpp_i<DPP_HMIRROR>((int)x));
+  x = max(x, (uint32_t)dpp_i<DPP_MIRROR>((int)x));
+  return max(max((uint32_t)__builtin_amdgcn_readlane((int)x, 0), (uint32_t)__builtin_amdgcn_readlane((int)x, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)x, 32), (uint32_t)__builtin_amdgcn_readlane((int)x, 48)));
+}
+
 template <typename T>
 __device__ __forceinline__ void publish_stats(ThrShared& th, uint32_t tkey, float c, int nc, int x,
                                               bool match, u64* stat, u64* sxw) {
   const int tid = threadIdx.x;
   const int wv = tid >> 6;
+  const int lane = tid & 63;
   const unsigned seg = list_cap<T>() / TNW;
   const unsigned nw = th.wcnt[wv];
   if (tid < REG_NC) {
@@ -2424,23 +2443,62 @@ __device__ __forceinline__ void publish_stats(ThrShared& th, uint32_t tkey, floa
   }
   if (tid == 0) th.csx = 0ull;
   __syncthreads();
-  const typename LE<T>::E* lst = list_of<T>(th);
-  for (unsigned i = (tid & 63); i < nw; i += 64) {
-    const typename LE<T>::E en = lst[wv * seg + i];
-    const uint32_t k = LE<T>::key(en);
-    if (k >= tkey) atomicMax(&th.cmax[LE<T>::index(en, wv) / CHUNK], k);
+  const typename LE<T>::E* lst = list_of<T>(th) + wv * seg;
+  // the window's chunk when all its kept entries share one (-1: none kept,
+  // -2: several)
+  auto window_chunk = [&](int cc) -> int {
+    const uint64_t live = __ballot(cc >= 0);
+    if (!live) return -1;
+    const int c0 = __builtin_amdgcn_readlane(cc, (int)__builtin_ctzll(live));
+    return __ballot(cc >= 0 && cc != c0) ? -2 : c0;
+  };
+  for (unsigned b0 = 0; b0 < nw; b0 += 64) {
+    const unsigned i = b0 + lane;
+    uint32_t k = 0u;
+    int cc = -1;
+    if (i < nw) {
+      const typename LE<T>::E en = lst[i];
+      const uint32_t kk = lkey<T>(en);
+      if (kk >= tkey) {
+        k = kk;
+        cc = LE<T>::index(en, wv) / CHUNK;
+      }
+    }
+    const int wc = window_chunk(cc);
+    if (wc >= 0) {
+      const uint32_t km = wave_max_u32(k);
+      if (lane == 0) atomicMax(&th.cmax[wc], km);
+    } else if (wc == -2 && cc >= 0) {
+      atomicMax(&th.cmax[cc], k);
+    }
   }
   __syncthreads();
   const int xc = x >= 0 ? x / CHUNK : -1;
-  for (unsigned i = (tid & 63); i < nw; i += 64) {
-    const typename LE<T>::E en = lst[wv * seg + i];
-    const uint32_t k = LE<T>::key(en);
-    if (k >= tkey) {
-      const int e = LE<T>::index(en, wv);
-      const int cc = e / CHUNK;
-      const unsigned long long fx = fixmass(term(keyv<T>(k), keyv<T>(th.cmax[cc]), c));
+  for (unsigned b0 = 0; b0 < nw; b0 += 64) {
+    const unsigned i = b0 + lane;
+    unsigned long long fx = 0ull, fs = 0ull;
+    int cc = -1;
+    if (i < nw) {
+      const typename LE<T>::E en = lst[i];
+      const uint32_t k = lkey<T>(en);
+      if (k >= tkey) {
+        const int e = LE<T>::index(en, wv);
+        cc = e / CHUNK;
+        fx = fixmass(term(keyv<T>(k), keyv<T>(th.cmax[cc]), c));
+        if (cc == xc && (match ? e < x : e != x)) fs = fx;
+      }
+    }
+    const int wc = window_chunk(cc);
+    if (wc >= 0) {
+      const unsigned long long sw = readlane_u64(wave_scan_u64(fx), 63);
+      const unsigned long long sx = wc == xc ? readlane_u64(wave_scan_u64(fs), 63) : 0ull;
+      if (lane == 0) {
+        atomicAdd(&th.csum[wc], sw);
+        if (sx) atomicAdd(&th.csx, sx);
+      }
+    } else if (wc == -2 && cc >= 0) {
       atomicAdd(&th.csum[cc], fx);
-      if (cc == xc && (match ? e < x : e != x)) atomicAdd(&th.csx, fx);
+      if (fs) atomicAdd(&th.csx, fs);
     }
   }
   __syncthreads();
@@ -2530,25 +2588,35 @@ __device__ __forceinline__ bool row_threshold(const T* __restrict__ rp, int V, b
   // number above the capacity when a segment overflowed.
   constexpr unsigned SEG = list_cap<T>() / TNW;
   auto fill_list = [&](float vlo) -> unsigned {
-    typename LE<T>::E* lst = list_of<T>(th) + (unsigned)(tid >> 6) * SEG;
+    using E = typename LE<T>::E;
+    E* lst = list_of<T>(th) + (unsigned)(tid >> 6) * SEG;
+    E* sink = reinterpret_cast<E*>(&th.sink[lane]);
     unsigned wc = 0u;
     each_w([&](const uint4& x, int e0) {
       float v[VEC];
-      int cnt = 0;
       unpack_word<T>(x, v);
+      float wm = v[0];
 #pragma unroll
-      for (int h = 0; h < VEC; ++h) cnt += v[h] >= vlo ? 1 : 0;
-      if (__ballot(cnt != 0)) {
+      for (int h = 1; h < VEC; ++h) wm = __builtin_fmaxf(wm, v[h]);
+      if (__ballot(wm >= vlo)) {
+        int cnt = 0;
+#pragma unroll
+        for (int h = 0; h < VEC; ++h) cnt += v[h] >= vlo ? 1 : 0;
         const int inc = wave_scan_add(cnt);
-        unsigned pos = wc + (unsigned)(inc - cnt);
+        const unsigned tot = (unsigned)__builtin_amdgcn_readlane(inc, 63);
+        if (wc + tot <= SEG) {
+          // every value is written, a candidate to its place and the rest to
+          // the lane's sink slot (no branch per value)
+          unsigned pos = wc + (unsigned)(inc - cnt);
 #pragma unroll
-        for (int h = 0; h < VEC; ++h) {
-          if (v[h] >= vlo) {
-            if (pos < SEG) lst[pos] = LE<T>::make(vkey<T>(v[h]), e0 + h);
-            ++pos;
+          for (int h = 0; h < VEC; ++h) {
+            const bool hit = v[h] >= vlo;
+            E* at = hit ? lst + pos : sink;
+            *at = LE<T>::make(__float_as_uint(v[h] + 0.f), e0 + h);
+            pos += hit ? 1u : 0u;
           }
         }
-        wc += (unsigned)__builtin_amdgcn_readlane(inc, 63);
+        wc += tot;
       }
     });
     if (lane == 0) th.wcnt[tid >> 6] = wc;
