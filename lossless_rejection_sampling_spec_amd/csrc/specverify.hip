@@ -158,6 +158,12 @@ struct Params {
   int H;          // helper workgroups per request (nc, or 0 for the greedy entry)
   int greedy_entry;
   int dsplit;     // draft-logit rows are read by draft strips of their own
+  // batches of more than 64 requests (the kernels instantiated with E = 16):
+  // k_order's table of the requests in launch order (request, cu0, cu1,
+  // class | valid << 2) and each request's offsets verdict; smaller batches
+  // look requests up in place
+  int32_t* order;   // [batch][4]
+  int32_t* okb;
 };
 
 // ---------------------------------------------------------------------------
@@ -1825,10 +1831,13 @@ __device__ __forceinline__ void helper(const Params& P, int b, int cu0, int k, i
 // last producer (merge, draws) then overlaps later requests' producers, and
 // the call ends on the cheapest chains.
 //
-// Every wave finds the request at its launch position on its own: E
-// consecutive requests per lane (E = 1 for batches of up to 64, else 16),
-// their offsets, temperatures and draft kinds loaded together (one round trip,
-// indices clamped into the batch), classes counted by ballots and DPP scans.
+// In a batch of up to 64 requests every wave finds the request at its launch
+// position on its own: one request per lane, its offsets, temperature and
+// draft kind loaded together (one round trip), classes counted by ballots and
+// DPP scans.  A larger batch (kernels instantiated with E = 16) has k_order
+// write the table once per call: sixteen requests per lane looked up in every
+// workgroup cost more than the table's launch as soon as the grid holds
+// thousands of workgroups.
 // A request is valid when its offsets pass req_valid and its first draft row
 // cu[b] - b is not below any earlier request's cu[e] - e.  That also puts cu[b]
 // above every earlier offset, so neither the target rows nor the draft rows of
@@ -1866,6 +1875,17 @@ __device__ __forceinline__ int wave_scan_max(int x) {   // inclusive, over the w
 
 template <int E>
 __device__ __forceinline__ ReqPos req_at(const Params& P, int pos) {
+  if constexpr (E > 1) {   // batches of more than 64: the table k_order wrote
+    const int32_t* r = P.order + 4 * pos;
+    ReqPos R;
+    R.b = ldu(r);
+    R.cu0 = ldu(r + 1);
+    R.cu1 = ldu(r + 2);
+    const int w = ldu(r + 3);
+    R.cls = w & 3;
+    R.valid = (w & 4) != 0;
+    return R;
+  }
   const int lane = threadIdx.x & 63;
   const int B = P.batch;
   const int i0 = lane * E;
@@ -1948,6 +1968,7 @@ __device__ __forceinline__ ReqPos req_at(const Params& P, int pos) {
 // wave-level load of the offsets for the largest cu[i] - i before b.
 template <int E>
 __device__ __forceinline__ bool offsets_ok(const Params& P, int b, int cu0, int cu1) {
+  if constexpr (E > 1) return ldu(P.okb + b) != 0;   // k_order's verdict
   const int i0 = (threadIdx.x & 63) * E;
   int m = INT32_MIN;
 #pragma unroll
@@ -1957,6 +1978,64 @@ __device__ __forceinline__ bool offsets_ok(const Params& P, int b, int cu0, int 
   }
   const int ra = __builtin_amdgcn_readlane(wave_scan_max(m), 63);
   return cu0 >= 0 && cu0 - b >= ra && req_valid(P, b, cu0, cu1, cu1 - cu0 - 1);
+}
+
+// The requests in launch order, once per call, for batches of more than 64
+// requests (one workgroup of 1,024 threads, thread t for request t): the
+// classes req_at sorts by (0 sampled with draft rows, 1 other sampled, 2
+// greedy; request order within a class), each request's place in that order,
+// and its offsets verdict (cu[t] - t at or above every earlier one, and the
+// checks of req_valid) -- what req_at and offsets_ok find in place for small
+// batches.  The workgroups of the later kernels then find their request with
+// one scalar load.
+__global__ __launch_bounds__(1024) void k_order(const Params P) {
+  __shared__ int wsum[3][16];
+  __shared__ int wmax[16];
+  const int t = threadIdx.x;
+  const int lane = t & 63, wv = t >> 6;
+  const int B = P.batch;
+  int cl = 3, cu0 = 0, cu1 = 0, fd = INT32_MIN;
+  if (t < B) {
+    cu0 = P.cu[t];
+    cu1 = P.cu[t + 1];
+    if (P.greedy_entry) {
+      cl = 2;
+    } else {
+      const float T = P.temp[t];
+      const int kd = P.kind[t];
+      cl = !(T >= FLT_MIN) ? 2 : (kd == SV_DRAFT_LOGITS || kd == SV_DRAFT_PROBS) ? 0 : 1;
+    }
+    fd = first_drow(cu0, t);
+  }
+  const int s0 = wave_scan_add(cl == 0 ? 1 : 0);
+  const int s1 = wave_scan_add(cl == 1 ? 1 : 0);
+  const int s2 = wave_scan_add(cl == 2 ? 1 : 0);
+  const int mx = wave_scan_max(fd);
+  const int before = __builtin_amdgcn_update_dpp(INT32_MIN, mx, 0x138, 0xf, 0xf, false);  // wave_shr:1
+  if (lane == 63) {
+    wsum[0][wv] = s0;
+    wsum[1][wv] = s1;
+    wsum[2][wv] = s2;
+    wmax[wv] = mx;
+  }
+  __syncthreads();
+  int b0 = 0, b1 = 0, b2 = 0, n0 = 0, n1 = 0, ra = before;
+  for (int q = 0; q < 16; ++q) {
+    if (q < wv) {
+      b0 += wsum[0][q];
+      b1 += wsum[1][q];
+      b2 += wsum[2][q];
+      ra = max(ra, wmax[q]);
+    }
+    n0 += wsum[0][q];
+    n1 += wsum[1][q];
+  }
+  if (t < B) {
+    const int pos = cl == 0 ? b0 + s0 - 1 : cl == 1 ? n0 + b1 + s1 - 1 : n0 + n1 + b2 + s2 - 1;
+    const bool valid = cu0 >= 0 && cu0 - t >= ra && req_valid(P, t, cu0, cu1, cu1 - cu0 - 1);
+    *reinterpret_cast<int4*>(P.order + 4 * pos) = make_int4(t, cu0, cu1, cl | (valid ? 4 : 0));
+    P.okb[t] = valid ? 1 : 0;
+  }
 }
 
 template <typename TT, typename TD, bool AL, int E>
@@ -3012,7 +3091,7 @@ __global__ void k_fill_zero(uint4* p, size_t n16, unsigned char* tail, size_t nt
 // host side
 // ---------------------------------------------------------------------------
 struct Layout {
-  size_t cst, dst, rx, dec, res, thr_t, thr_d, pq, ctl, total;
+  size_t cst, dst, rx, dec, res, thr_t, thr_d, pq, ctl, order, okb, total;
 };
 
 static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -3036,6 +3115,8 @@ static bool layout(int batch, int total_rows, int vocab, int max_k, Layout& L, i
   L.thr_t = o; o = align_up(o + R * sizeof(u64));
   L.thr_d = o; o = align_up(o + D1 * sizeof(u64));
   L.pq = o; o = align_up(o + B * (size_t)(2 * max_k + 1) * sizeof(u64));
+  L.order = o; o = align_up(o + B * 4 * sizeof(int32_t));
+  L.okb = o; o = align_up(o + B * sizeof(int32_t));
   L.total = o;
   return true;
 }
@@ -3055,6 +3136,12 @@ static int launch_all(Params P, bool sampled, bool filters, bool aligned, hipStr
   const long long g = verify_grid<TT>(P);
   if (g >= (1LL << 31)) return SV_ERR_SHAPE;
   const size_t lds = (size_t)8 * (2 * P.max_k + 1) * P.nc;
+  if (P.batch > 64) {
+    hipLaunchKernelGGL(k_order, dim3(1), dim3(1024), 0, st, P);
+  } else {
+    P.order = nullptr;
+    P.okb = nullptr;
+  }
   // requests per lane when finding a request by launch position or checking
   // its offsets
   if (P.pen) {
@@ -3124,6 +3211,8 @@ static void carve(Params& P, void* ws, const Layout& L) {
   P.thr_d = (u64*)(w + L.thr_d);
   P.pq = (u64*)(w + L.pq);
   P.ctl = (u64*)(w + L.ctl);
+  P.order = (int32_t*)(w + L.order);
+  P.okb = (int32_t*)(w + L.okb);
 }
 
 
