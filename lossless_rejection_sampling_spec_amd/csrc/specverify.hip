@@ -784,7 +784,12 @@ __device__ __forceinline__ CStat chunk_stats(Seg<T>& sg, bool greedy, float tau,
       accx = 0.f;
 #pragma unroll
       for (int i = 0; i < EPT; ++i) {
-        const float e = term(sg.at(i), m, c);
+        // a rare path: each value passes an empty asm statement with the
+        // running sums, so its term is formed after the previous one is
+        // added instead of every term being held at once
+        float v = sg.at(i);
+        asm volatile("" : "+v"(v), "+v"(acc), "+v"(accx));
+        const float e = term(v, m, c);
         acc += e;
         accx += (xl < 0) ? 0.f
                 : before ? ((strided_index<T>(i) < xl) ? e : 0.f)
