@@ -421,6 +421,36 @@ def test_offsets_going_back_draft_logit_requests():
     check(synth.make(1, seed=4, batch=8, vocab=9000))
 
 
+def test_offsets_going_back_in_a_large_batch():
+    """Broken offsets in a batch of more than 64 requests, whose workgroups
+    take their request and its offsets verdict from the table written once
+    per call: every draft kind, greedy rows and top-k / top-p filters (so the
+    threshold kernel reads the verdicts too), with a request of negative
+    length followed by one that starts below it, and a request longer than
+    max_k followed by two whose offsets it overruns.  Every request gets the
+    oracle's verdict, and a clean large call on the same workspace follows."""
+    rng = np.random.default_rng(77)
+    B, V = 96, 9000
+    ks = rng.integers(0, 7, size=B)
+    kinds = rng.choice(np.array([synth.LOGITS, synth.PROBS, synth.ONEHOT, synth.MATCH]),
+                       size=B).astype(np.int32)
+    temps = rng.uniform(0.5, 1.2, size=B).astype(np.float32)
+    temps[rng.random(B) < 0.2] = 0.0
+    top_k = rng.choice(np.array([0, 0, 20]), size=B).astype(np.int32)
+    top_p = rng.choice(np.array([1.0, 0.9]), size=B).astype(np.float32)
+    w = synth.build(31, seed=77, batch=B, vocab=V, ks=ks, target_dtype=synth.BF16,
+                    draft_dtype=synth.BF16, kinds=kinds, temps=temps, sigma=0.5, top_k=top_k,
+                    top_p=top_p, max_k=6, name="large batch, broken offsets")
+    cu = w.cu_seqlens.copy()
+    cu[21] = cu[20] - 1          # request 20: negative length; 21 starts below 20's offset
+    cu[71] = cu[70] + 9          # request 70: k = 8 > max_k; 71 and 72 overrun
+    w.cu_seqlens = cu
+    gpu, counts = check(w)
+    bad = [int(r) for r in np.flatnonzero(gpu["status"] == oracle.ROW_BAD_K)]
+    assert bad == [20, 21, 70, 71, 72], bad
+    check(synth.make(3, seed=6, batch=80, vocab=9000))
+
+
 def test_residual_paths_around_the_peer_limit():
     """Rows of 32 chunks (the helpers of a rejection exchange their residual
     masses and the chunk's holder draws) and of 33 chunks (one helper gathers
