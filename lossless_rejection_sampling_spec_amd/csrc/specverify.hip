@@ -322,6 +322,14 @@ template <typename T>
 __device__ __forceinline__ void load_contig(const T* __restrict__ cp, int n, bool al, float fill,
                                             Seg<T>& s) {
   constexpr int VEC = VT<T>::VEC;
+  if (al && n >= CHUNK) {
+    // a whole chunk (uniform): one base address, the words at immediate
+    // offsets, nothing to clamp or mask
+    const uint4* base = reinterpret_cast<const uint4*>(cp + (int)threadIdx.x * EPT);
+#pragma unroll
+    for (int i = 0; i < Seg<T>::NV; ++i) s.q[i] = base[i];
+    return;
+  }
   load_words<T>(cp, n, al, fill, [](int i) { return (int)threadIdx.x * EPT + i * VEC; }, s);
 }
 
