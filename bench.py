@@ -40,8 +40,8 @@ MAX_POOL = 16          # host cores a one-GPU machine gives this job
 # Keyed by the SHA-256 of the kernel source the counters were taken on: for
 # any other source the figure is stale and the bench reports null.
 TRAFFIC_BYTES: dict = {
-    # FETCH 71,932.3 KiB x 1.99963 + WRITE 347.6 KiB x 1.0 per launch
-    "d6e7b987517b052461a72e5cd2b1900cbfb2609869bc01a842d857cc5ffe2bb4": 147646266,
+    # FETCH 71,889.5 KiB x 1.99963 + WRITE 346.6 KiB x 1.0 per launch
+    "0750c227cce21dd05100ef86b9b3c3ed4c763e2db4e00f7b03287371429c1c96": 147557602,
 }
 
 # Workloads besides the headline one: (config, steps per repetition, label).
