@@ -257,6 +257,37 @@ def test_edge_masked_tokens_and_faults():
     check_edge(_one(rows, kind=synth.PROBS, drafts=[3, 77], draft=probs2, u=[0.999, 0.5, 0.5]))
 
 
+def test_edge_faults_in_filtered_rows():
+    """Filtered rows whose statistics the threshold kernel would publish from
+    its candidate list, with faults: a NaN in a target row, +inf in the bonus
+    row or a NaN in a draft-logit row leaves the row unpublished and the
+    request NONFINITE (the verify kernel's own row pass finds it); a draft id
+    far below the cut is masked by the filter and rejected.  Both element
+    types, top-k, top-p and both."""
+    rng = np.random.default_rng(12)
+    V = 9000
+    rows = np.round(rng.normal(0, 2, size=(3, V)), 2)
+    draft = rows[:2] + rng.normal(0, 0.3, size=(2, V))
+    xs = [int(np.argmax(draft[0])), int(np.argmax(draft[1]))]
+    low = int(np.argmin(rows[0]))
+    for dtype in (synth.BF16, synth.F32):
+        for K, P in ((20, 1.0), (0, 0.9), (50, 0.95)):
+            say(f"faults in filtered rows dtype={dtype} K={K} P={P}")
+            kw = dict(T=0.9, kind=synth.LOGITS, dtype=dtype, ddtype=dtype, top_k=K, top_p=P)
+            nan_t = rows.copy()
+            nan_t[1, 4321] = np.nan
+            check_edge(_one(nan_t, drafts=xs, draft=draft, **kw), oracle.ROW_NONFINITE)
+            inf_t = rows.copy()
+            inf_t[2, 17] = np.inf
+            check_edge(_one(inf_t, drafts=xs, draft=draft, **kw), oracle.ROW_NONFINITE)
+            nan_d = draft.copy()
+            nan_d[0, 99] = np.nan
+            check_edge(_one(rows, drafts=xs, draft=nan_d, **kw), oracle.ROW_NONFINITE)
+            gpu = check_edge(_one(rows, drafts=[low, xs[1]], draft=draft, u=[0.5, 0.5, 0.5], **kw),
+                             oracle.ROW_OK)
+            assert int(gpu["accepted"][0]) == 0
+
+
 def test_edge_onehot_and_degenerate_targets():
     V = 8200
     rows = np.full((3, V), -np.inf)
