@@ -42,6 +42,8 @@ MAX_POOL = 16          # host cores a one-GPU machine gives this job
 TRAFFIC_BYTES: dict = {
     # FETCH 71,889.5 KiB x 1.99963 + WRITE 346.6 KiB x 1.0 per launch
     "0750c227cce21dd05100ef86b9b3c3ed4c763e2db4e00f7b03287371429c1c96": 147557602,
+    # the same source with a comment changed (the built library is byte-identical)
+    "af37787b3794f5b618de248a8afc3c7c822f5bb2c6fc417db510f4443964ea01": 147557602,
 }
 
 # Workloads besides the headline one: (config, steps per repetition, label).

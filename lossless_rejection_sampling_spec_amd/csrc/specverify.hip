@@ -2145,9 +2145,11 @@ __global__ __launch_bounds__(WG, 4) void k_verify(const Params P) {
 // each pass.  The passes are VALU-bound (a wave64 vector instruction takes 4
 // cycles), so the full-row work is kept to a few instructions per value:
 //
-// * top-k (K <= 1,024): the K-th largest of the 1,024 per-thread maxima is a
-//   lower bound of the K-th largest value; one compare pass appends every
-//   value at or above it to a list in LDS, and the select runs on the list;
+// * top-k (K <= 1,024): each wave's r-th largest thread maximum, r =
+//   ceil(K / 16), found by a ballot binary search over the key bits, and the
+//   smallest of the 16 is a lower bound of the K-th largest value; one compare
+//   pass appends every value at or above it to a list in LDS, and the select
+//   runs on the list;
 // * top-p without top-k: one pass sums the integer masses per thread in fp64
 //   for the total Z (fp32 sums of the eight values of a 128-bit word, added
 //   in fp64 in a fixed order: deterministic, within about 1e-7), and adds
@@ -2165,8 +2167,14 @@ __global__ __launch_bounds__(WG, 4) void k_verify(const Params P) {
 // kept in registers.  A row whose list would overflow a segment, or whose
 // bound is -inf, takes full-row radix passes instead.  A level's histogram has
 // HCOPY copies, one per lane of a half wave, so lanes of one LDS atomic share
-// an address only when they are 32 apart and agree on the digit; one wave then
-// picks the digit from suffix sums of the merged bins.
+// an address only when they are 32 apart and agree on the digit (a list of at
+// most LIST_SMALL entries adds into one copy); one wave then picks the digit
+// from suffix sums of the merged bins.
+//
+// A threshold found on a list also gives the row's chunk statistics: every
+// kept value is on the list, so the workgroup publishes them in the words the
+// verify kernel's producers would write (publish_stats) and marks the row's
+// threshold word; that kernel then leaves the row alone, which is read once.
 constexpr int TW = 1024;          // threads of a threshold workgroup
 constexpr int TNW = TW / 64;
 constexpr int THR_NL = 16;        // 128-bit words per thread of a row kept in registers
